@@ -1,0 +1,22 @@
+"""Oracle for windowed grouped-query attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the ``smoke()`` check of ``__graft_entry__`` and the
+CPU-baseline leg of ``bench.py`` may import anything from this package.  The
+product path (the ``windowed_gqa_kv_amd`` binding, the C-ABI library and its
+HIP kernels) never imports, calls or links it, and this package imports
+nothing from the product path.
+
+``attention``  plain materialized float64 attention (NumPy), the definition.
+``brute``      the same definition with scalar Python loops, for tiny shapes.
+"""
+
+from .materialized import (  # noqa: F401
+    allowed,
+    attention,
+    prefill,
+    decode,
+    append_kv,
+    sink_logits,
+    softcap_fn,
+)
+from . import brute  # noqa: F401
