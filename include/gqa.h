@@ -1,0 +1,167 @@
+/*
+ * gqa.h -- C ABI of the MI355X (gfx950) windowed grouped-query attention library.
+ *
+ * Library: libgqa_mi355x.so (hand-written HIP kernels; no host fallback).
+ *
+ * What is computed.  For batch b, query head h (K/V head g = h / G, G =
+ * num_heads / kv_num_heads, K/V never copied per query head), query row i at
+ * absolute position p = q_offset_b + i, and key slot j at position j, key j is
+ * ALLOWED iff
+ *     j < valid_b  and  (not causal or j <= p)  and  (W == -1 or p - j < W).
+ * x_ij = scale * <q_i, k_j>, then x_ij = c * tanh(x_ij / c) when softcap c > 0.
+ *     O_i = sum_{j allowed} e^{x_ij} v_j / (sum_{j allowed} e^{x_ij} + [sink] e^{s_h})
+ * and O_i = 0 exactly when no key is allowed.  Sources (page, section):
+ *   - head sharing without copies, [B,H,L,D] / [B,L,H*D] layouts, softcap,
+ *     nonpad_kv_seqlen, zero rows, fp32 accumulation: "Attention Kernel
+ *     Design" (onnx-light-cpu), sections "Layouts and semantics" and
+ *     "Scheduling, precision, and invariants";
+ *   - window in absolute positions, decode rows at (total - curr) + i, sink
+ *     in the denominator only: "[NPUW] Support GQA sliding-window and
+ *     smooth-softmax in DecomposeGQA", sections "Sliding window
+ *     (local_window_size)" and "smooth_softmax / head_sink";
+ *   - bottom-right causal alignment and the KV cache as concatenation of past
+ *     and step: "onnx: import GroupQueryAttention decode steps and its
+ *     internal rotary", section "What changed".
+ *
+ * Conventions shared by every entry point.
+ *   Ownership:  every device buffer belongs to the caller.  The library never
+ *               allocates device memory; it owns only the host-side plan.
+ *   Asynchrony: calls enqueue work on `hip_stream` (a hipStream_t; NULL = the
+ *               default stream) and return; GQA_OK means "enqueued".
+ *   Validation: everything checkable on the host is checked before any launch.
+ *               On error nothing is enqueued, the status says which class of
+ *               error, and gqa_last_error() returns a message naming the
+ *               argument (thread-local; valid until the next failing call on
+ *               the same thread).
+ *   Tensors:    gqa_tensor = base pointer + element strides for batch, head and
+ *               sequence; the head dimension is contiguous.  [B,H,L,D] and
+ *               [B,L,H*D] are both expressible.  Base pointers must be 16-byte
+ *               aligned and strides multiples of 16 bytes / element size.
+ *   Device-side lengths: seqlens_k / nonpad_kv_seqlen live in device memory
+ *               and cannot be checked on the host.  A value out of range makes
+ *               every output row of that batch exactly zero (and append_kv
+ *               skip that batch); no access leaves the tensors' extents.
+ *   Threads:    a plan is immutable after gqa_plan(); it may be used from
+ *               several threads/streams at once if each call gets its own
+ *               workspace.
+ */
+#ifndef GQA_MI355X_H
+#define GQA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gqa_plan_s* gqa_plan_t;
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1, /* malformed argument or attribute combination */
+  GQA_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels cover */
+  GQA_ERR_CAPACITY = 3,    /* a size exceeds the plan's maxima or the cache */
+  GQA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} gqa_status;
+
+/* Element type of Q, K, V, O and the cache (all equal).  Mirrors the
+ * FLOAT / FLOAT16 / BFLOAT16 type set of "Attention Kernel Design". */
+typedef enum { GQA_F32 = 0, GQA_F16 = 1, GQA_BF16 = 2 } gqa_dtype;
+
+/* Node attributes.  Mirrors GroupQueryAttention's attribute set as the pages
+ * describe it (num_heads, kv_num_heads, scale, local_window_size, softcap,
+ * smooth_softmax, head_sink) plus the causal flag of ONNX Attention. */
+typedef struct {
+  int32_t num_heads;         /* Hq > 0 */
+  int32_t kv_num_heads;      /* Hkv > 0, Hq % Hkv == 0 */
+  int32_t head_size;         /* D: multiple of 8, 8..256 (V has the same D) */
+  float scale;               /* > 0; 0 selects 1/sqrt(D) */
+  int32_t local_window_size; /* -1 = off; W >= 1 = keys kept per query, self included */
+  float softcap;             /* 0 = off; c > 0 applies c*tanh(x/c) to scaled logits */
+  int32_t smooth_softmax;    /* 0/1: extra logit 0 in the denominator when no head_sink */
+  int32_t use_head_sink;     /* 0/1: a per-query-head fp32 sink logit array is passed */
+  int32_t is_causal;         /* 1 = bottom-right causal band; 0 only with W == -1 */
+  gqa_dtype dtype;           /* element type of every tensor argument */
+} gqa_attrs;
+
+/* A strided 4-D view [B][H][L][D] with a contiguous last dimension.  Strides
+ * are in elements.  [B,L,H*D] is stride_b = L*H*D, stride_h = D, stride_s = H*D. */
+typedef struct {
+  void* data;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_s;
+} gqa_tensor;
+
+/* Validate attributes and size limits; build an immutable plan.
+ * max_batch, max_q_len (prefill Lq / decode curr) and max_kv_len (prefill Lk /
+ * decode capacity) bound every later call and size the workspace.
+ * Following the descriptor/plan split of "Attention Kernel Design", section
+ * "Descriptor and invocation plan".  Host only; touches no device.
+ * Errors: INVALID_ARG (bad attribute or pairing), UNSUPPORTED (head_size). */
+gqa_status gqa_plan(const gqa_attrs* attrs, int32_t max_batch, int32_t max_q_len,
+                    int64_t max_kv_len, gqa_plan_t* out_plan);
+
+/* Release a plan (NULL is ignored).  Must not race with calls using it. */
+void gqa_plan_destroy(gqa_plan_t plan);
+
+/* Bytes of device workspace gqa_decode needs at the plan's maxima (split-KV
+ * partial results).  gqa_prefill and gqa_append_kv need none.  0 for NULL. */
+size_t gqa_workspace_size(gqa_plan_t plan);
+
+/* Prompt attention on an empty past ("Attention Kernel Design", sections
+ * "Layouts and semantics" and "Compute paths"; bottom-right band of "onnx:
+ * import GroupQueryAttention decode steps ...", section "What changed").
+ *   q   [B, Hq,  Lq, D]   k, v [B, Hkv, Lk, D]   out [B, Hq, Lq, D]
+ *   q_offset = Lk - Lq (rows with negative positions see nothing -> 0).
+ *   nonpad_kv_seqlen: device int64 [B] or NULL (NULL = Lk for every batch);
+ *     keys j >= nonpad_b are masked; the causal offset is unchanged.
+ *   head_sink: device fp32 [Hq]; non-NULL iff attrs.use_head_sink.
+ *   workspace/ws_bytes: unused (may be NULL/0).
+ * B == 0 or Lq == 0 is a no-op.  Lk == 0 writes zeros.
+ * Errors: INVALID_ARG (NULL/misaligned/negative sizes, sink pairing),
+ *   CAPACITY (B, Lq or Lk above the plan maxima), UNSUPPORTED (stride
+ *   alignment), HIP (launch failure). */
+gqa_status gqa_prefill(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk,
+                       gqa_tensor q, gqa_tensor k, gqa_tensor v, gqa_tensor out,
+                       const int64_t* nonpad_kv_seqlen, const float* head_sink,
+                       void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Append curr new K/V rows per (batch, KV head) to the cache: row t goes to
+ * slot total_b - curr + t, total_b = seqlens_k[b] + 1 (present =
+ * concat(past, step), "onnx: import GroupQueryAttention decode steps ...",
+ * section "What changed").
+ *   k_new, v_new [B, Hkv, curr, D]   k_cache, v_cache [B, Hkv, capacity, D]
+ *   seqlens_k: device int32 [B] (a [B,1] array is the same memory).
+ * A batch with total_b < curr or total_b > capacity is skipped.
+ * Errors: INVALID_ARG, CAPACITY (curr > capacity or above plan maxima),
+ *   UNSUPPORTED, HIP. */
+gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                         gqa_tensor k_new, gqa_tensor v_new,
+                         gqa_tensor k_cache, gqa_tensor v_cache,
+                         const int32_t* seqlens_k, void* hip_stream);
+
+/* Single- or multi-token decode of curr new tokens against a cache that
+ * already holds them (call gqa_append_kv first).  Query row t of batch b sits
+ * at position total_b - curr + t; keys are the slots [0, total_b) ("[NPUW]
+ * Support GQA sliding-window ...", section "Sliding window
+ * (local_window_size)"; causal inside the step: row t sees new tokens <= t).
+ *   q, out [B, Hq, curr, D]   k_cache, v_cache [B, Hkv, capacity, D]
+ *   seqlens_k: device int32 [B]; head_sink as in gqa_prefill.
+ *   workspace: device, >= gqa_workspace_size(plan) bytes, 16-byte aligned,
+ *     owned by this call until it completes on the stream.
+ * Errors: INVALID_ARG (incl. workspace too small), CAPACITY, UNSUPPORTED, HIP. */
+gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                      gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                      const int32_t* seqlens_k, const float* head_sink,
+                      void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_MI355X_H */

@@ -1,0 +1,165 @@
+"""The C-ABI library on the host: it loads, exports exactly what include/gqa.h
+declares, and rejects every malformed call before touching a device.
+
+None of these calls reaches a kernel launch (each fails validation first), so
+they run without a GPU.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from windowed_gqa_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+FAKE = 1 << 20  # a 16-byte aligned non-NULL address; never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", src)))
+
+
+def attrs(**kw):
+    base = dict(num_heads=8, kv_num_heads=2, head_size=128, scale=0.0, local_window_size=-1,
+                softcap=0.0, smooth_softmax=0, use_head_sink=0, is_causal=1, dtype=B.GQA_BF16)
+    base.update(kw)
+    return B.gqa_attrs(**base)
+
+
+def plan(**kw):
+    st, h = B.gqa_plan(attrs(**kw), 4, 16, 1024)
+    assert st == B.GQA_OK, B.gqa_last_error()
+    return h
+
+
+def t(ptr=FAKE, sb=1024 * 128 * 8, sh=1024 * 128, ss=128):
+    return B.gqa_tensor(ptr, sb, sh, ss)
+
+
+def test_library_exports_exactly_the_header():
+    lib = B.load()
+    names = declared_functions()
+    assert names == sorted(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines()
+                      if l.split()[-2] in ("T", "W") and l.split()[-1].startswith("gqa_"))
+    assert exported == names
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(num_heads=0), B.GQA_ERR_INVALID_ARG, "num_heads"),
+    (dict(kv_num_heads=0), B.GQA_ERR_INVALID_ARG, "kv_num_heads"),
+    (dict(num_heads=8, kv_num_heads=3), B.GQA_ERR_INVALID_ARG, "multiple"),
+    (dict(head_size=100), B.GQA_ERR_UNSUPPORTED, "head_size"),
+    (dict(head_size=512), B.GQA_ERR_UNSUPPORTED, "head_size"),
+    (dict(scale=-1.0), B.GQA_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("nan")), B.GQA_ERR_INVALID_ARG, "scale"),
+    (dict(local_window_size=0), B.GQA_ERR_INVALID_ARG, "local_window_size"),
+    (dict(local_window_size=-2), B.GQA_ERR_INVALID_ARG, "local_window_size"),
+    (dict(softcap=-1.0), B.GQA_ERR_INVALID_ARG, "softcap"),
+    (dict(softcap=float("inf")), B.GQA_ERR_INVALID_ARG, "softcap"),
+    (dict(smooth_softmax=2), B.GQA_ERR_INVALID_ARG, "smooth_softmax"),
+    (dict(use_head_sink=5), B.GQA_ERR_INVALID_ARG, "use_head_sink"),
+    (dict(is_causal=0, local_window_size=4), B.GQA_ERR_INVALID_ARG, "is_causal"),
+    (dict(dtype=7), B.GQA_ERR_INVALID_ARG, "dtype"),
+])
+def test_plan_rejects_bad_attributes(kw, status, needle):
+    st, h = B.gqa_plan(attrs(**kw), 4, 16, 1024)
+    assert st == status and h is None
+    assert needle in B.gqa_last_error()
+
+
+def test_plan_rejects_bad_limits_and_null():
+    assert B.gqa_plan(attrs(), 0, 16, 1024)[0] == B.GQA_ERR_INVALID_ARG
+    assert B.gqa_plan(attrs(), 4, 16, 1 << 31)[0] == B.GQA_ERR_UNSUPPORTED
+    lib = B.load()
+    assert lib.gqa_plan(None, 4, 16, 1024, ctypes.byref(B.gqa_plan_t())) == B.GQA_ERR_INVALID_ARG
+    assert "attrs" in B.gqa_last_error()
+
+
+def test_workspace_size_and_destroy():
+    h = plan()
+    assert B.gqa_workspace_size(h) > 0
+    B.gqa_plan_destroy(h)
+    assert B.gqa_workspace_size(None) == 0
+    B.gqa_plan_destroy(None)
+    # fp32 runs the generic kernels, which need no workspace
+    h = plan(dtype=B.GQA_F32)
+    assert B.gqa_workspace_size(h) == 0
+    B.gqa_plan_destroy(h)
+
+
+def _prefill(h, Bn=2, Lq=8, Lk=8, q=None, k=None, v=None, o=None, nonpad=None, sink=None):
+    return B.gqa_prefill(h, Bn, Lq, Lk, q or t(), k or t(), v or t(), o or t(), nonpad, sink,
+                         None, 0, None)
+
+
+def test_prefill_validation():
+    h = plan()
+    assert _prefill(None) == B.GQA_ERR_INVALID_ARG
+    assert _prefill(h, Bn=-1) == B.GQA_ERR_INVALID_ARG
+    assert _prefill(h, Bn=5) == B.GQA_ERR_CAPACITY and "max_batch" in B.gqa_last_error()
+    assert _prefill(h, Lq=17) == B.GQA_ERR_CAPACITY and "max_q_len" in B.gqa_last_error()
+    assert _prefill(h, Lk=1025) == B.GQA_ERR_CAPACITY and "max_kv_len" in B.gqa_last_error()
+    assert _prefill(h, q=t(ptr=0)) == B.GQA_ERR_INVALID_ARG and "q.data" in B.gqa_last_error()
+    assert _prefill(h, k=t(ptr=FAKE + 2)) == B.GQA_ERR_UNSUPPORTED and "aligned" in B.gqa_last_error()
+    assert _prefill(h, v=t(ss=100)) == B.GQA_ERR_UNSUPPORTED and "multiples" in B.gqa_last_error()
+    assert _prefill(h, o=t(sh=-128)) == B.GQA_ERR_INVALID_ARG and "negative" in B.gqa_last_error()
+    assert _prefill(h, sink=ctypes.c_void_p(FAKE)) == B.GQA_ERR_INVALID_ARG
+    assert "use_head_sink" in B.gqa_last_error()
+    # empty work is a no-op that succeeds without touching the device
+    assert _prefill(h, Bn=0) == B.GQA_OK
+    assert _prefill(h, Lq=0) == B.GQA_OK
+    hs = plan(use_head_sink=1)
+    assert _prefill(hs) == B.GQA_ERR_INVALID_ARG and "head_sink is NULL" in B.gqa_last_error()
+
+
+def test_append_validation():
+    h = plan()
+    s = ctypes.c_void_p(FAKE)
+    def app(Bn=2, curr=1, cap=64, seq=s, **kw):
+        return B.gqa_append_kv(h, Bn, curr, cap, kw.get("kn", t()), kw.get("vn", t()),
+                               kw.get("kc", t()), kw.get("vc", t()), seq, None)
+    assert app(curr=17) == B.GQA_ERR_CAPACITY
+    assert app(cap=1025) == B.GQA_ERR_CAPACITY
+    assert app(curr=8, cap=4) == B.GQA_ERR_CAPACITY and "capacity" in B.gqa_last_error()
+    assert app(seq=None) == B.GQA_ERR_INVALID_ARG and "seqlens_k" in B.gqa_last_error()
+    assert app(kc=t(ptr=0)) == B.GQA_ERR_INVALID_ARG and "k_cache" in B.gqa_last_error()
+    assert app(Bn=0) == B.GQA_OK
+
+
+def test_decode_validation():
+    h = plan()
+    ws = B.gqa_workspace_size(h)
+    s = ctypes.c_void_p(FAKE)
+    def dec(Bn=2, curr=1, cap=64, seq=s, wsp=FAKE, wsb=ws, sink=None):
+        return B.gqa_decode(h, Bn, curr, cap, t(), t(), t(), t(), seq, sink,
+                            ctypes.c_void_p(wsp) if wsp else None, wsb, None)
+    assert dec(curr=17) == B.GQA_ERR_CAPACITY
+    assert dec(seq=None) == B.GQA_ERR_INVALID_ARG
+    assert dec(wsp=0) == B.GQA_ERR_INVALID_ARG and "workspace" in B.gqa_last_error()
+    assert dec(wsb=16) == B.GQA_ERR_INVALID_ARG and "workspace" in B.gqa_last_error()
+    assert dec(wsp=FAKE + 8) == B.GQA_ERR_INVALID_ARG and "aligned" in B.gqa_last_error()
+    assert dec(sink=ctypes.c_void_p(FAKE)) == B.GQA_ERR_INVALID_ARG
+    assert dec(curr=0) == B.GQA_OK
+
+
+def test_last_error_is_thread_local_and_specific():
+    import threading
+    B.gqa_plan(attrs(num_heads=0), 1, 1, 1)
+    msg = []
+    th = threading.Thread(target=lambda: msg.append(B.gqa_last_error()))
+    th.start()
+    th.join()
+    assert msg == [""]
+    assert "num_heads" in B.gqa_last_error()

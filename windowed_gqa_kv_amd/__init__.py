@@ -3,17 +3,10 @@
 The compute lives in a C-ABI shared library of hand-written HIP kernels
 (``libgqa_mi355x.so``, built from ``csrc/``; declarations in ``include/gqa.h``
 at the repository root).  ``binding`` marshals torch device tensors into that
-ABI; it performs no arithmetic of its own and raises if the library is
-missing.
+ABI; it performs no arithmetic of its own, loads the library on first use and
+raises if it is missing.
 """
 
-from . import inputs, work  # noqa: F401  (pure host helpers, no device code)
+from . import binding, inputs, work  # noqa: F401
 
-__all__ = ["inputs", "work", "binding"]
-
-
-def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    raise AttributeError(name)
+__all__ = ["binding", "inputs", "work"]

@@ -1,0 +1,263 @@
+"""ctypes binding of libgqa_mi355x (declarations: include/gqa.h).
+
+Argument marshalling only: torch tensors are turned into pointers, element
+strides and the current HIP stream; every step of the computation runs in the
+library's HIP kernels.  torch is used for device memory (outputs, workspace)
+and streams.  If the library is missing, ``load()`` raises -- there is no
+fallback path.
+
+The C entry points are exposed under their own names (``gqa_plan``,
+``gqa_prefill``, ...) taking ctypes structures; ``Plan`` wraps them for torch
+tensors.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_mi355x.so")
+
+GQA_OK = 0
+GQA_ERR_INVALID_ARG = 1
+GQA_ERR_UNSUPPORTED = 2
+GQA_ERR_CAPACITY = 3
+GQA_ERR_HIP = 4
+STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
+                3: "GQA_ERR_CAPACITY", 4: "GQA_ERR_HIP"}
+
+GQA_F32, GQA_F16, GQA_BF16 = 0, 1, 2
+DTYPE_CODES = {"f32": GQA_F32, "f16": GQA_F16, "bf16": GQA_BF16}
+
+EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
+            "gqa_append_kv", "gqa_decode", "gqa_last_error")
+
+
+class gqa_attrs(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("kv_num_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("local_window_size", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
+        ("smooth_softmax", ctypes.c_int32),
+        ("use_head_sink", ctypes.c_int32),
+        ("is_causal", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+    ]
+
+
+class gqa_tensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_s", ctypes.c_int64),
+    ]
+
+
+gqa_plan_t = ctypes.c_void_p
+_lib = None
+
+
+def load():
+    """Load libgqa_mi355x.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m windowed_gqa_kv_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    T, P, I32, I64, S = gqa_tensor, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.gqa_plan.argtypes = [ctypes.POINTER(gqa_attrs), I32, I32, I64, ctypes.POINTER(gqa_plan_t)]
+    lib.gqa_plan.restype = ctypes.c_int
+    lib.gqa_plan_destroy.argtypes = [gqa_plan_t]
+    lib.gqa_plan_destroy.restype = None
+    lib.gqa_workspace_size.argtypes = [gqa_plan_t]
+    lib.gqa_workspace_size.restype = S
+    lib.gqa_prefill.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P, S, P]
+    lib.gqa_prefill.restype = ctypes.c_int
+    lib.gqa_append_kv.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P]
+    lib.gqa_append_kv.restype = ctypes.c_int
+    lib.gqa_decode.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P, S, P]
+    lib.gqa_decode.restype = ctypes.c_int
+    lib.gqa_last_error.argtypes = []
+    lib.gqa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# The C entry points under their own names (ctypes arguments, status returned)
+# ---------------------------------------------------------------------------
+def gqa_plan(attrs: gqa_attrs, max_batch: int, max_q_len: int, max_kv_len: int):
+    """Returns (status, plan handle or None)."""
+    h = gqa_plan_t()
+    st = load().gqa_plan(ctypes.byref(attrs), max_batch, max_q_len, max_kv_len, ctypes.byref(h))
+    return st, (h if st == GQA_OK else None)
+
+
+def gqa_plan_destroy(plan) -> None:
+    load().gqa_plan_destroy(plan)
+
+
+def gqa_workspace_size(plan) -> int:
+    return int(load().gqa_workspace_size(plan))
+
+
+def gqa_prefill(plan, B, Lq, Lk, q, k, v, out, nonpad_kv_seqlen, head_sink, workspace, ws_bytes,
+                stream) -> int:
+    return load().gqa_prefill(plan, B, Lq, Lk, q, k, v, out, nonpad_kv_seqlen, head_sink,
+                              workspace, ws_bytes, stream)
+
+
+def gqa_append_kv(plan, B, curr, capacity, k_new, v_new, k_cache, v_cache, seqlens_k, stream) -> int:
+    return load().gqa_append_kv(plan, B, curr, capacity, k_new, v_new, k_cache, v_cache,
+                                seqlens_k, stream)
+
+
+def gqa_decode(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, workspace,
+               ws_bytes, stream) -> int:
+    return load().gqa_decode(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
+                             head_sink, workspace, ws_bytes, stream)
+
+
+def gqa_last_error() -> str:
+    return load().gqa_last_error().decode()
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor convenience layer
+# ---------------------------------------------------------------------------
+class GQAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def check(status: int) -> None:
+    if status != GQA_OK:
+        raise GQAError(status, gqa_last_error())
+
+
+def tensor_view(t, heads: Optional[int] = None) -> gqa_tensor:
+    """gqa_tensor for a [B, H, L, D] tensor, or a [B, L, H*D] tensor with ``heads``."""
+    if t.dim() == 4:
+        sb, sh, ss, sd = t.stride()
+    elif t.dim() == 3:
+        if heads is None:
+            raise ValueError("a [B, L, H*D] tensor needs the head count")
+        sb, ss, sd = t.stride()
+        sh = t.shape[2] // heads
+    else:
+        raise ValueError("expected a 4-D [B,H,L,D] or 3-D [B,L,H*D] tensor")
+    if sd != 1:
+        raise ValueError("the head dimension must be contiguous")
+    return gqa_tensor(t.data_ptr(), sb, sh, ss)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_TORCH_CODE = None
+
+
+def _dtype_code(t):
+    import torch
+    global _TORCH_CODE
+    if _TORCH_CODE is None:
+        _TORCH_CODE = {torch.float32: GQA_F32, torch.float16: GQA_F16, torch.bfloat16: GQA_BF16}
+    return _TORCH_CODE[t.dtype]
+
+
+class Plan:
+    """An immutable attention plan (``gqa_plan``) driven with torch tensors."""
+
+    def __init__(self, num_heads: int, kv_num_heads: int, head_size: int, *, dtype: str,
+                 scale: float = 0.0, local_window_size: int = -1, softcap: float = 0.0,
+                 smooth_softmax: bool = False, use_head_sink: bool = False,
+                 is_causal: bool = True, max_batch: int = 1, max_q_len: int = 1,
+                 max_kv_len: int = 1):
+        self.attrs = gqa_attrs(num_heads, kv_num_heads, head_size, scale, local_window_size,
+                               softcap, int(smooth_softmax), int(use_head_sink), int(is_causal),
+                               DTYPE_CODES[dtype])
+        self.dtype = dtype
+        self.num_heads, self.kv_num_heads, self.head_size = num_heads, kv_num_heads, head_size
+        self._h = None
+        st, h = gqa_plan(self.attrs, max_batch, max_q_len, max_kv_len)
+        check(st)
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            _lib.gqa_plan_destroy(self._h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def workspace_size(self) -> int:
+        return gqa_workspace_size(self._h)
+
+    def new_workspace(self, device="cuda"):
+        import torch
+        return torch.empty(max(16, self.workspace_size()), dtype=torch.uint8, device=device)
+
+    def _check_dtype(self, *ts):
+        want = DTYPE_CODES[self.dtype]
+        for t in ts:
+            if t is not None and _dtype_code(t) != want:
+                raise TypeError(f"tensor dtype {t.dtype} does not match the plan's {self.dtype}")
+
+    def prefill(self, q, k, v, out=None, *, nonpad_kv_seqlen=None, head_sink=None,
+                layout="bhsd", stream=None):
+        """q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (layout "bhsd") or [B,L,H*D] ("bshd")."""
+        import torch
+        self._check_dtype(q, k, v)
+        if out is None:
+            out = torch.empty_like(q)
+        if layout == "bhsd":
+            B, _, Lq, _ = q.shape
+            Lk = k.shape[2]
+            qv, kv_, vv, ov = (tensor_view(x) for x in (q, k, v, out))
+        else:
+            B, Lq, _ = q.shape
+            Lk = k.shape[1]
+            qv, ov = tensor_view(q, self.num_heads), tensor_view(out, self.num_heads)
+            kv_, vv = tensor_view(k, self.kv_num_heads), tensor_view(v, self.kv_num_heads)
+        check(gqa_prefill(self._h, B, Lq, Lk, qv, kv_, vv, ov, _ptr(nonpad_kv_seqlen),
+                          _ptr(head_sink), None, 0, _stream(stream)))
+        return out
+
+    def append_kv(self, k_new, v_new, k_cache, v_cache, seqlens_k, *, stream=None):
+        self._check_dtype(k_new, v_new, k_cache, v_cache)
+        B, _, curr, _ = k_new.shape
+        check(gqa_append_kv(self._h, B, curr, k_cache.shape[2], tensor_view(k_new),
+                            tensor_view(v_new), tensor_view(k_cache), tensor_view(v_cache),
+                            _ptr(seqlens_k), _stream(stream)))
+
+    def decode(self, q, k_cache, v_cache, seqlens_k, out=None, *, head_sink=None,
+               workspace=None, stream=None):
+        import torch
+        self._check_dtype(q, k_cache, v_cache)
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.new_workspace(q.device)
+        B, _, curr, _ = q.shape
+        check(gqa_decode(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_cache),
+                         tensor_view(v_cache), tensor_view(out), _ptr(seqlens_k), _ptr(head_sink),
+                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                         _stream(stream)))
+        return out

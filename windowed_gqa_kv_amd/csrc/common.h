@@ -1,0 +1,162 @@
+// Device-side building blocks shared by the gfx950 kernels of libgqa_mi355x.
+//
+// Everything here is written for CDNA4 (gfx950, wave64).  Element types are
+// carried as raw 16-bit storage (bf16 / fp16) or float; arithmetic is fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// ---------------------------------------------------------------------------
+// Vector types matching the MFMA operand registers.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Arguments common to every attention kernel (passed by value).
+// Strides are in elements; the head dimension is contiguous.
+// mode 0 (prompt):  q_offset = Lk - Lq; valid = nonpad[b] (or Lk).
+// mode 1 (decode):  total = seqlens[b] + 1; q_offset = total - Lq; valid = total.
+// An out-of-range device length turns that batch's rows into zeros.
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  const int64_t* nonpad;   // mode 0, may be null
+  const int32_t* seqlens;  // mode 1
+  const float* head_sink;  // null: sink logit 0 when use_sink
+  int32_t B, Hq, Hkv, G, D;
+  int32_t Lq;       // prompt rows, or curr for decode
+  int32_t Lk;       // keys in K/V, or cache capacity
+  int32_t mode;
+  int32_t causal;
+  int32_t window;   // -1 = off
+  int32_t use_sink;
+  float scale_log2;     // scale * log2(e)
+  float scale_over_cap; // scale / softcap (softcap > 0 only)
+  float cap_log2;       // softcap * log2(e)
+};
+
+struct BatchSpan {
+  int q_off;  // absolute position of query row 0
+  int valid;  // keys [0, valid) exist
+};
+
+__device__ __forceinline__ BatchSpan batch_span(const AttnArgs& a, int b) {
+  BatchSpan s;
+  if (a.mode == 0) {
+    int64_t n = a.nonpad ? a.nonpad[b] : (int64_t)a.Lk;
+    bool ok = n >= 0 && n <= a.Lk;
+    s.valid = ok ? (int)n : 0;
+    s.q_off = a.Lk - a.Lq;
+  } else {
+    int64_t total = (int64_t)a.seqlens[b] + 1;
+    bool ok = total >= a.Lq && total <= a.Lk;
+    s.valid = ok ? (int)total : 0;
+    s.q_off = ok ? (int)(total - a.Lq) : 0;
+  }
+  return s;
+}
+
+// Allowed keys of the query at absolute position p form [lo, hi] (empty when
+// lo > hi): every constraint is a half-line in the key index.
+__device__ __forceinline__ int row_lo(const AttnArgs& a, int p) {
+  return a.window < 0 ? 0 : max(0, p - a.window + 1);
+}
+__device__ __forceinline__ int row_hi(const AttnArgs& a, int p, int valid) {
+  return a.causal ? min(p, valid - 1) : valid - 1;
+}
+
+// Sink logit of query head h in log2 units.
+__device__ __forceinline__ float sink_log2(const AttnArgs& a, int h) {
+  return a.head_sink ? a.head_sink[h] * kLog2e : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Scalar helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// tanh from the identity tanh(y) = 1 - 2 / (e^{2y} + 1) for |y| >= 1/4, and
+// its Taylor series through y^9 below that (truncation < 1e-8 relative there).
+__device__ __forceinline__ float tanh_f32(float y) {
+  float ay = fabsf(y);
+  if (ay < 0.25f) {
+    float y2 = y * y;
+    float poly = 1.0f + y2 * (-1.0f / 3.0f + y2 * (2.0f / 15.0f +
+                 y2 * (-17.0f / 315.0f + y2 * (62.0f / 2835.0f))));
+    return y * poly;
+  }
+  float e = fast_exp2(2.0f * kLog2e * ay);
+  float r = 1.0f - 2.0f / (e + 1.0f);
+  return copysignf(r, y);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  _Float16 x;
+  __builtin_memcpy(&x, &h, 2);
+  return (float)x;
+}
+template <bool IS_BF16>
+__device__ __forceinline__ float half_to_f32(uint16_t h) {
+  if constexpr (IS_BF16) return bf16_to_f32(h); else return f16_to_f32(h);
+}
+
+// Round-to-nearest-even narrowing (v_cvt_pk_bf16_f32 / v_cvt_f16_f32).
+template <bool IS_BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (IS_BF16) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    uint16_t ua, ub;
+    __builtin_memcpy(&ua, &a, 2);
+    __builtin_memcpy(&ub, &b, 2);
+    return (uint32_t)ua | ((uint32_t)ub << 16);
+  } else {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    uint16_t ua, ub;
+    __builtin_memcpy(&ua, &a, 2);
+    __builtin_memcpy(&ub, &b, 2);
+    return (uint32_t)ua | ((uint32_t)ub << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level reductions (wave64).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Value of lane l ^ 32 (the other half-wave).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+}  // namespace gqa

@@ -1,0 +1,286 @@
+// C ABI of libgqa_mi355x: attribute validation, the immutable plan, per-call
+// argument checks and kernel dispatch.
+//
+// The split between a validated descriptor (built once) and a per-call plan
+// (layout and strides, head mapping, lengths) follows "Attention Kernel
+// Design", section "Descriptor and invocation plan"; explicit failure with a
+// specific message for every unsupported or inconsistent input follows the
+// same page, section "Scheduling, precision, and invariants", and the
+// "rejected with specific messages" convention of "onnx: import
+// GroupQueryAttention decode steps and its internal rotary", section "What
+// changed".  Nothing here touches the device except the kernel launches.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gqa.h"
+#include "kernels.h"
+
+#define GQA_API extern "C" __attribute__((visibility("default")))
+
+struct gqa_plan_s {
+  gqa_attrs attrs;
+  float scale;  // resolved (0 -> 1/sqrt(D))
+  int G;
+  int32_t max_batch;
+  int32_t max_q_len;
+  int64_t max_kv_len;
+  size_t ws_bytes;
+};
+
+namespace {
+
+constexpr int64_t kMaxLen = int64_t(1) << 30;  // keeps every position in int32 arithmetic
+
+thread_local std::string g_err;
+
+gqa_status fail(gqa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+int elem_size(gqa_dtype t) { return t == GQA_F32 ? 4 : 2; }
+
+gqa_status check_tensor(const char* name, const gqa_tensor& t, int esz) {
+  if (t.data == nullptr) return fail(GQA_ERR_INVALID_ARG, "%s.data is NULL", name);
+  if (reinterpret_cast<uintptr_t>(t.data) % 16 != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "%s.data must be 16-byte aligned", name);
+  if (t.stride_b < 0 || t.stride_h < 0 || t.stride_s < 0)
+    return fail(GQA_ERR_INVALID_ARG, "%s has a negative stride", name);
+  const int64_t q = 16 / esz;
+  if (t.stride_b % q || t.stride_h % q || t.stride_s % q)
+    return fail(GQA_ERR_UNSUPPORTED, "%s strides must be multiples of %lld elements (16 bytes)", name,
+                (long long)q);
+  return GQA_OK;
+}
+
+gqa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GQA_OK;
+  return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+gqa::AttnArgs make_args(const gqa_plan_s* p, const gqa_tensor& q, const gqa_tensor& k,
+                        const gqa_tensor& v, const gqa_tensor& o, int B, int Lq, int64_t Lk, int mode) {
+  gqa::AttnArgs a{};
+  a.q = q.data;
+  a.k = k.data;
+  a.v = v.data;
+  a.o = o.data;
+  a.q_sb = q.stride_b; a.q_sh = q.stride_h; a.q_ss = q.stride_s;
+  a.k_sb = k.stride_b; a.k_sh = k.stride_h; a.k_ss = k.stride_s;
+  a.v_sb = v.stride_b; a.v_sh = v.stride_h; a.v_ss = v.stride_s;
+  a.o_sb = o.stride_b; a.o_sh = o.stride_h; a.o_ss = o.stride_s;
+  a.B = B;
+  a.Hq = p->attrs.num_heads;
+  a.Hkv = p->attrs.kv_num_heads;
+  a.G = p->G;
+  a.D = p->attrs.head_size;
+  a.Lq = Lq;
+  a.Lk = (int32_t)Lk;
+  a.mode = mode;
+  a.causal = p->attrs.is_causal;
+  a.window = p->attrs.local_window_size;
+  a.use_sink = (p->attrs.use_head_sink || p->attrs.smooth_softmax) ? 1 : 0;
+  const float log2e = 1.4426950408889634f;
+  a.scale_log2 = p->scale * log2e;
+  a.scale_over_cap = p->attrs.softcap > 0 ? p->scale / p->attrs.softcap : 0.0f;
+  a.cap_log2 = p->attrs.softcap > 0 ? p->attrs.softcap * log2e : 0.0f;
+  return a;
+}
+
+gqa_status check_sink(const gqa_plan_s* p, const float* head_sink) {
+  if (p->attrs.use_head_sink && head_sink == nullptr)
+    return fail(GQA_ERR_INVALID_ARG, "use_head_sink is set but head_sink is NULL");
+  if (!p->attrs.use_head_sink && head_sink != nullptr)
+    return fail(GQA_ERR_INVALID_ARG, "head_sink passed but the plan has use_head_sink = 0");
+  return GQA_OK;
+}
+
+}  // namespace
+
+GQA_API gqa_status gqa_plan(const gqa_attrs* attrs, int32_t max_batch, int32_t max_q_len,
+                            int64_t max_kv_len, gqa_plan_t* out_plan) {
+  if (out_plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "out_plan is NULL");
+  *out_plan = nullptr;
+  if (attrs == nullptr) return fail(GQA_ERR_INVALID_ARG, "attrs is NULL");
+  const gqa_attrs& a = *attrs;
+  if (a.num_heads <= 0) return fail(GQA_ERR_INVALID_ARG, "num_heads must be > 0 (got %d)", a.num_heads);
+  if (a.kv_num_heads <= 0)
+    return fail(GQA_ERR_INVALID_ARG, "kv_num_heads must be > 0 (got %d)", a.kv_num_heads);
+  if (a.num_heads % a.kv_num_heads != 0)
+    return fail(GQA_ERR_INVALID_ARG, "num_heads (%d) must be a multiple of kv_num_heads (%d)",
+                a.num_heads, a.kv_num_heads);
+  if (a.num_heads > 65535) return fail(GQA_ERR_UNSUPPORTED, "num_heads above 65535");
+  if (a.dtype != GQA_F32 && a.dtype != GQA_F16 && a.dtype != GQA_BF16)
+    return fail(GQA_ERR_INVALID_ARG, "dtype %d is not F32, F16 or BF16", (int)a.dtype);
+  if (a.head_size < 8 || a.head_size > 256 || a.head_size % 8 != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "head_size %d: need a multiple of 8 in [8, 256]", a.head_size);
+  if (!(a.scale >= 0.0f) || std::isinf(a.scale))
+    return fail(GQA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 = 1/sqrt(head_size))");
+  if (a.local_window_size != -1 && a.local_window_size < 1)
+    return fail(GQA_ERR_INVALID_ARG, "local_window_size must be -1 (off) or >= 1 (got %d)",
+                a.local_window_size);
+  if (!(a.softcap >= 0.0f) || std::isinf(a.softcap))
+    return fail(GQA_ERR_INVALID_ARG, "softcap must be finite and >= 0 (0 = off)");
+  if (a.smooth_softmax != 0 && a.smooth_softmax != 1)
+    return fail(GQA_ERR_INVALID_ARG, "smooth_softmax must be 0 or 1");
+  if (a.use_head_sink != 0 && a.use_head_sink != 1)
+    return fail(GQA_ERR_INVALID_ARG, "use_head_sink must be 0 or 1");
+  if (a.is_causal != 0 && a.is_causal != 1) return fail(GQA_ERR_INVALID_ARG, "is_causal must be 0 or 1");
+  if (!a.is_causal && a.local_window_size != -1)
+    return fail(GQA_ERR_INVALID_ARG, "local_window_size needs is_causal = 1 (the window is one-sided)");
+  if (max_batch < 1 || max_q_len < 1 || max_kv_len < 1)
+    return fail(GQA_ERR_INVALID_ARG, "max_batch, max_q_len and max_kv_len must be >= 1");
+  if (max_batch > 65535) return fail(GQA_ERR_UNSUPPORTED, "max_batch above 65535");
+  if (max_q_len > kMaxLen || max_kv_len > kMaxLen)
+    return fail(GQA_ERR_UNSUPPORTED, "sequence lengths above 2^30");
+
+  gqa_plan_s* p = new (std::nothrow) gqa_plan_s;
+  if (p == nullptr) return fail(GQA_ERR_INVALID_ARG, "out of host memory");
+  p->attrs = a;
+  p->scale = a.scale > 0.0f ? a.scale : 1.0f / std::sqrt((float)a.head_size);
+  p->G = a.num_heads / a.kv_num_heads;
+  p->max_batch = max_batch;
+  p->max_q_len = max_q_len;
+  p->max_kv_len = max_kv_len;
+  p->ws_bytes = 0;
+  if (gqa::decode_mfma_supported(a.dtype, a.head_size)) {
+    gqa::DecodeGeometry geo = gqa::decode_geometry(max_batch, a.kv_num_heads, p->G, max_q_len, max_kv_len,
+                                                   a.local_window_size, a.is_causal, a.head_size);
+    p->ws_bytes = geo.ws_floats * sizeof(float);
+  }
+  *out_plan = p;
+  return GQA_OK;
+}
+
+GQA_API void gqa_plan_destroy(gqa_plan_t plan) { delete plan; }
+
+GQA_API size_t gqa_workspace_size(gqa_plan_t plan) { return plan ? plan->ws_bytes : 0; }
+
+GQA_API gqa_status gqa_prefill(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk, gqa_tensor q,
+                               gqa_tensor k, gqa_tensor v, gqa_tensor out,
+                               const int64_t* nonpad_kv_seqlen, const float* head_sink,
+                               void* workspace, size_t ws_bytes, void* hip_stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || Lq < 0 || Lk < 0) return fail(GQA_ERR_INVALID_ARG, "B, Lq and Lk must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (Lq > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "Lq = %d exceeds the plan's max_q_len %d", Lq, plan->max_q_len);
+  if (Lk > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "Lk = %lld exceeds the plan's max_kv_len %lld", (long long)Lk,
+                (long long)plan->max_kv_len);
+  gqa_status st = check_sink(plan, head_sink);
+  if (st != GQA_OK) return st;
+  if (B == 0 || Lq == 0) return GQA_OK;
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("q", q, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
+  if (Lk > 0) {
+    if ((st = check_tensor("k", k, esz)) != GQA_OK) return st;
+    if ((st = check_tensor("v", v, esz)) != GQA_OK) return st;
+  }
+  gqa::AttnArgs a = make_args(plan, q, k, v, out, B, Lq, Lk, 0);
+  a.nonpad = nonpad_kv_seqlen;
+  a.head_sink = head_sink;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int dtype = (int)plan->attrs.dtype;
+  hipError_t e;
+  if (Lk > 0 && gqa::prefill_mfma_supported(dtype, plan->attrs.head_size))
+    e = gqa::launch_prefill_mfma(a, dtype, plan->attrs.softcap > 0, stream);
+  else
+    e = gqa::launch_attn_generic(a, dtype, stream);
+  return hip_status(e, "prefill launch");
+}
+
+GQA_API gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                 gqa_tensor k_new, gqa_tensor v_new, gqa_tensor k_cache,
+                                 gqa_tensor v_cache, const int32_t* seqlens_k, void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (curr > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the plan's max_q_len %d", curr, plan->max_q_len);
+  if (capacity > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
+                (long long)plan->max_kv_len);
+  if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  if (B == 0 || curr == 0) return GQA_OK;
+  if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const int esz = elem_size(plan->attrs.dtype);
+  gqa_status st;
+  if ((st = check_tensor("k_new", k_new, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("v_new", v_new, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, esz)) != GQA_OK) return st;
+  gqa::AppendArgs a{};
+  a.k_new = k_new.data;
+  a.v_new = v_new.data;
+  a.k_cache = k_cache.data;
+  a.v_cache = v_cache.data;
+  a.kn_sb = k_new.stride_b * esz; a.kn_sh = k_new.stride_h * esz; a.kn_ss = k_new.stride_s * esz;
+  a.vn_sb = v_new.stride_b * esz; a.vn_sh = v_new.stride_h * esz; a.vn_ss = v_new.stride_s * esz;
+  a.kc_sb = k_cache.stride_b * esz; a.kc_sh = k_cache.stride_h * esz; a.kc_ss = k_cache.stride_s * esz;
+  a.vc_sb = v_cache.stride_b * esz; a.vc_sh = v_cache.stride_h * esz; a.vc_ss = v_cache.stride_s * esz;
+  a.seqlens = seqlens_k;
+  a.B = B;
+  a.Hkv = plan->attrs.kv_num_heads;
+  a.curr = curr;
+  a.row_bytes = plan->attrs.head_size * esz;
+  a.capacity = (int32_t)capacity;
+  return hip_status(gqa::launch_append_kv(a, reinterpret_cast<hipStream_t>(hip_stream)), "append_kv launch");
+}
+
+GQA_API gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                              gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                              const int32_t* seqlens_k, const float* head_sink, void* workspace,
+                              size_t ws_bytes, void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (curr > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the plan's max_q_len %d", curr, plan->max_q_len);
+  if (capacity > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
+                (long long)plan->max_kv_len);
+  if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  gqa_status st = check_sink(plan, head_sink);
+  if (st != GQA_OK) return st;
+  if (B == 0 || curr == 0) return GQA_OK;
+  if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("q", q, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
+  gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
+  a.seqlens = seqlens_k;
+  a.head_sink = head_sink;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int dtype = (int)plan->attrs.dtype;
+  if (gqa::decode_mfma_supported(dtype, plan->attrs.head_size)) {
+    gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, capacity, a.window, a.causal,
+                                                   a.D);
+    const size_t need = geo.ws_floats * sizeof(float);
+    if (workspace == nullptr || ws_bytes < need)
+      return fail(GQA_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
+                  workspace ? "" : ", NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if ((int64_t)B * a.Hkv * geo.row_tiles > 65535)
+      return fail(GQA_ERR_UNSUPPORTED, "B * kv_num_heads * row tiles above 65535");
+    return hip_status(gqa::launch_decode_mfma(a, dtype, plan->attrs.softcap > 0, geo,
+                                              reinterpret_cast<float*>(workspace), stream),
+                      "decode launch");
+  }
+  return hip_status(gqa::launch_attn_generic(a, dtype, stream), "decode launch");
+}
+
+GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }

@@ -1,0 +1,55 @@
+// Host-side launchers of the gfx950 kernels (internal to libgqa_mi355x).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace gqa {
+
+enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Any dtype, any head size (multiple of 8, <= 256), prompt or decode mode:
+// one wavefront per query row, fp32 throughout.  Writes every output row.
+hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t stream);
+
+// Flash-style prompt attention on bf16/fp16 MFMA (32x32x16).  Head sizes 64
+// and 128.  Writes every output row.
+bool prefill_mfma_supported(int dtype, int head_size);
+hipError_t launch_prefill_mfma(const AttnArgs& a, int dtype, bool softcap, hipStream_t stream);
+
+// Split-KV decode on bf16/fp16 MFMA (16x16x32 for QK^T, 16x16x16 for PV):
+// one workgroup per (batch, KV head, 16-row tile, key chunk) writes an
+// fp32 partial (acc, max, sum); a combine kernel merges the partials, folds
+// the sink and writes O.  Head sizes 64, 128, 256.
+struct DecodeGeometry {
+  int rows;        // G * curr query rows per KV head
+  int row_tiles;   // ceil(rows / 16)
+  int chunk;       // keys per split
+  int splits;      // splits covering the longest possible key range
+  size_t ws_floats;
+};
+bool decode_mfma_supported(int dtype, int head_size);
+DecodeGeometry decode_geometry(int B, int Hkv, int G, int curr, int64_t capacity,
+                               int window, int causal, int head_size);
+hipError_t launch_decode_mfma(const AttnArgs& a, int dtype, bool softcap,
+                              const DecodeGeometry& geo, float* ws, hipStream_t stream);
+
+// KV-cache append: copy curr rows per (batch, KV head) to slots
+// total_b - curr ... total_b - 1 of the cache.
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  int64_t kn_sb, kn_sh, kn_ss;
+  int64_t vn_sb, vn_sh, vn_ss;
+  int64_t kc_sb, kc_sh, kc_ss;
+  int64_t vc_sb, vc_sh, vc_ss;
+  const int32_t* seqlens;
+  int32_t B, Hkv, curr, row_bytes;
+  int32_t capacity;
+};
+hipError_t launch_append_kv(const AppendArgs& a, hipStream_t stream);
+
+}  // namespace gqa
