@@ -1,0 +1,269 @@
+"""Benchmark of the windowed GQA hot path on one MI355X.
+
+Default workload: single-token decode, bf16, B=8, Hq=32, Hkv=8, D=128, KV
+capacity 4096, seqlens_k ~ integers[1024, 4096), smooth_softmax (zero sink),
+window off.  One step = the whole decode path for one batch: gqa_append_kv
+(the new token's K/V into the cache) then gqa_decode (split-KV attention +
+combine).  Inputs are resident in HBM before timing starts.  Every step
+works on a different replica of the KV cache (R replicas, >= 1 GiB in
+total), so a step cannot be served from the 256 MB Infinity Cache left warm
+by the previous one.
+
+Prints ONE JSON line.  `value` = algorithmic bytes of the step (K/V rows of
+the kept key range, Q, O, and the appended rows) / wall time per step.
+`roofline` is for the dominant kernel (gqa_decode), timed with HIP events on
+the stream it is launched on.  `cpu_baseline` times the float64 oracle on
+this host (the oracle as it stands, on a bounded number of full decode
+steps).  `extra` reports the prompt workloads (TFLOP/s against the bf16 MFMA
+peak) and the speculative-decode workload the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+       [--no-cpu-baseline] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "prefill TFLOP/s (%MFMA peak); decode KV-cache GB/s (%HBM peak), 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_1tok_bf16")
+    ap.add_argument("--replicas", type=int, default=0, help="KV replicas (0 = enough for 1 GiB)")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-steps", type=int, default=20)
+    return ap.parse_args()
+
+
+def _src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "windowed_gqa_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, workload: str, src_files):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = table.get(f"{kernel}/{workload}")
+    if not rec or rec.get("src_hash") != _src_hash(src_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def bench_decode(w, steps, warmup, replicas):
+    import torch
+    from windowed_gqa_kv_amd import binding, work
+    from windowed_gqa_kv_amd.inputs import generate
+
+    d = generate(w)
+    plan = binding.Plan(w.Hq, w.Hkv, w.D, dtype=w.dtype, scale=w.sm_scale, local_window_size=w.window,
+                        softcap=w.softcap, smooth_softmax=w.smooth_softmax, use_head_sink=w.head_sink,
+                        is_causal=w.causal, max_batch=w.B, max_q_len=w.Lq, max_kv_len=w.Lk)
+    kv_bytes = 2 * d["k_cache"].numel() * d["k_cache"].element_size()
+    R = replicas or max(2, -(-(1 << 30) // kv_bytes))
+    kc0, vc0 = d["k_cache"].cuda(), d["v_cache"].cuda()
+    caches = [(kc0.clone(), vc0.clone()) for _ in range(R)]
+    del kc0, vc0
+    q = d["q"].cuda()
+    kn, vn = d["k_new"].cuda(), d["v_new"].cuda()
+    seq = d["seqlens_k"].cuda()
+    sink = None if d["head_sink"] is None else d["head_sink"].cuda()
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(16, plan.workspace_size()), dtype=torch.uint8, device="cuda")
+
+    def step(i, ev=None):
+        kc, vc = caches[i % R]
+        plan.append_kv(kn, vn, kc, vc, seq)
+        if ev is not None:
+            ev[0].record()
+        plan.decode(q, kc, vc, seq, out, head_sink=sink, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(warmup):
+        step(i)
+    evs = _events(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    s = d["seqlens_k"].numpy()
+    dec_bytes = work.decode_bytes(s, w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window)
+    app_bytes = work.append_bytes(w.B, w.Hkv, w.Lq, w.D, w.dtype)
+    ms = (t1 - t0) * 1000.0 / steps
+    return dict(ms_per_step=ms, step_bytes=dec_bytes + app_bytes, kernel_ms=dec_ms,
+                kernel_bytes=dec_bytes, replicas=R, inputs=d)
+
+
+def bench_prefill(w, steps, warmup):
+    import torch
+    from windowed_gqa_kv_amd import binding, work
+    from windowed_gqa_kv_amd.inputs import generate
+
+    d = generate(w)
+    plan = binding.Plan(w.Hq, w.Hkv, w.D, dtype=w.dtype, scale=w.sm_scale, local_window_size=w.window,
+                        softcap=w.softcap, smooth_softmax=w.smooth_softmax, use_head_sink=w.head_sink,
+                        is_causal=w.causal, max_batch=w.B, max_q_len=w.Lq, max_kv_len=w.Lk)
+    q, k, v = d["q"].cuda(), d["k"].cuda(), d["v"].cuda()
+    nonpad = None if d["nonpad"] is None else d["nonpad"].cuda()
+    sink = None if d["head_sink"] is None else d["head_sink"].cuda()
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        plan.prefill(q, k, v, out, nonpad_kv_seqlen=nonpad, head_sink=sink)
+    evs = _events(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record()
+        plan.prefill(q, k, v, out, nonpad_kv_seqlen=nonpad, head_sink=sink)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    flops = work.prefill_flops(w.B, w.Hq, w.D, w.Lq, w.Lk, w.causal, w.window, w.nonpad)
+    kms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return dict(ms_per_step=(t1 - t0) * 1000.0 / steps, flops=flops, kernel_ms=kms)
+
+
+def cpu_baseline(w, d, budget_s=12.0):
+    """The float64 oracle on full decode steps of the same workload, repeated
+    until ~budget_s of CPU time; reported in the same unit (GB/s)."""
+    import numpy as np
+    import oracle
+    from windowed_gqa_kv_amd import work
+    from windowed_gqa_kv_amd.inputs import to_f64
+
+    s = d["seqlens_k"].numpy().astype(np.int64)
+    top = int(s.max()) + 1
+    kc = to_f64(d["k_cache"][:, :, :top])
+    vc = to_f64(d["v_cache"][:, :, :top])
+    kc, vc = oracle.append_kv(kc, vc, to_f64(d["k_new"]), to_f64(d["v_new"]), s)
+    q = to_f64(d["q"])
+    sink = to_f64(d["head_sink"])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode(q, kc, vc, s, scale=w.sm_scale, causal=w.causal, window=w.window,
+                      softcap=w.softcap, smooth_softmax=w.smooth_softmax, head_sink=sink)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    b = work.decode_bytes(s, w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window)
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{n} full decode steps of the same workload (append + decode, float64 "
+                      f"materialized oracle, {dt * 1e3:.1f} ms each)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the attention path has no multi-GPU mode "
+              f"(requested --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from windowed_gqa_kv_amd import binding
+    from windowed_gqa_kv_amd.inputs import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    byname = {w.name: w for w in WORKLOADS.values()}
+    w = byname[args.workload]
+    if w.kind != "decode":
+        print("the headline workload must be a decode workload", file=sys.stderr)
+        sys.exit(2)
+
+    r = bench_decode(w, args.steps, args.warmup, args.replicas)
+    value = r["step_bytes"] / (r["ms_per_step"] / 1e3) / 1e9
+    achieved = r["kernel_bytes"] / (r["kernel_ms"] / 1e3) / 1e9
+    dec_src = ["decode_mfma.hip", "common.h", "kernels.h"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1); KV cache rotated over "
+                f"{r['replicas']} replicas so no step reads a warm Infinity Cache)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "curr": w.Lq, "kv_capacity": w.Lk, "window": w.window,
+                   "seqlens_k": [int(x) for x in r["inputs"]["seqlens_k"].numpy()],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "gqa_decode (split + combine)",
+                     "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": _traffic("decode", w.name, dec_src),
+                     "kernel_ms": round(r["kernel_ms"], 5), "bytes_per_launch": r["kernel_bytes"]},
+    }
+
+    if not args.no_extra:
+        extra = []
+        for wid in (4,):
+            w4 = WORKLOADS[wid]
+            r4 = bench_decode(w4, args.extra_steps, 3, 0)
+            a4 = r4["kernel_bytes"] / (r4["kernel_ms"] / 1e3) / 1e9
+            extra.append({"workload": w4.name, "value": round(r4["step_bytes"] / (r4["ms_per_step"] / 1e3) / 1e9, 2),
+                          "unit": "GB/s", "ms_per_step": round(r4["ms_per_step"], 5),
+                          "roofline": {"bound": "hbm", "achieved": round(a4, 2), "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": round(a4 / PEAK_HBM_GBS, 4),
+                                       "kernel_ms": round(r4["kernel_ms"], 5)}})
+            del r4
+        for wid in (3, 5):
+            wp = WORKLOADS[wid]
+            rp = bench_prefill(wp, args.extra_steps, 3)
+            tf = rp["flops"] / (rp["kernel_ms"] / 1e3) / 1e12
+            extra.append({"workload": wp.name,
+                          "value": round(rp["flops"] / (rp["ms_per_step"] / 1e3) / 1e12, 2),
+                          "unit": "TFLOP/s", "ms_per_step": round(rp["ms_per_step"], 5),
+                          "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                       "kernel_ms": round(rp["kernel_ms"], 5), "flops_per_launch": rp["flops"]}})
+            torch.cuda.empty_cache()
+        line["extra"] = extra
+
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, r["inputs"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
