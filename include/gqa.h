@@ -106,8 +106,12 @@ gqa_status gqa_plan(const gqa_attrs* attrs, int32_t max_batch, int32_t max_q_len
 /* Release a plan (NULL is ignored).  Must not race with calls using it. */
 void gqa_plan_destroy(gqa_plan_t plan);
 
-/* Bytes of device workspace gqa_decode needs at the plan's maxima (split-KV
- * partial results).  gqa_prefill and gqa_append_kv need none.  0 for NULL. */
+/* Bytes of device workspace gqa_decode needs at the plan's maxima: per-row-
+ * tile arrival counters followed by the split-KV partial results.  The
+ * workspace must be zero-filled once before its first gqa_decode call; every
+ * completed call leaves the counters at zero again, so it can be reused by
+ * later calls (of any plan) without clearing.  gqa_prefill and gqa_append_kv
+ * need none.  0 for NULL. */
 size_t gqa_workspace_size(gqa_plan_t plan);
 
 /* Prompt attention on an empty past ("Attention Kernel Design", sections
@@ -150,7 +154,9 @@ gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capac
  *   q, out [B, Hq, curr, D]   k_cache, v_cache [B, Hkv, capacity, D]
  *   seqlens_k: device int32 [B]; head_sink as in gqa_prefill.
  *   workspace: device, >= gqa_workspace_size(plan) bytes, 16-byte aligned,
- *     owned by this call until it completes on the stream.
+ *     zero-filled before its first use (see gqa_workspace_size), owned by
+ *     this call until it completes on the stream; calls that overlap in time
+ *     must use different workspaces.
  * Errors: INVALID_ARG (incl. workspace too small), CAPACITY, UNSUPPORTED, HIP. */
 gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
                       gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,

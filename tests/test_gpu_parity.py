@@ -231,3 +231,44 @@ def test_repeat_runs_are_bitwise_identical(gpu):
     a, _, _ = gpu_decode(w, d)
     b, _, _ = gpu_decode(w, d)
     assert torch.equal(a, b)
+
+
+def test_decode_workspace_reuse_across_shapes(gpu):
+    """One zero-filled workspace serves many decode calls of different shapes
+    and plans: each call must leave its arrival counters at zero."""
+    import torch as _t
+    cases = [
+        Workload("reuse", "decode", "bf16", B=3, Hq=8, Hkv=2, D=128, Lq=1, Lk=900, window=-1,
+                 smooth_softmax=True, seqlens=("list", [10, 500, 899]), seed=21),
+        Workload("reuse", "decode", "bf16", B=2, Hq=16, Hkv=2, D=128, Lq=4, Lk=900, window=100,
+                 head_sink=True, seqlens=("list", [3, 700]), seed=22),
+        Workload("reuse", "decode", "bf16", B=4, Hq=8, Hkv=4, D=256, Lq=2, Lk=600, window=-1,
+                 softcap=20.0, seqlens=("list", [1, 64, 65, 599]), seed=23),
+    ]
+    plans = [make_plan(w) for w in cases]
+    ws = _t.zeros(max(p.workspace_size() for p in plans), dtype=_t.uint8, device="cuda")
+    for rep in range(3):
+        for w, plan in zip(cases, plans):
+            d = generate(w)
+            kc, vc = d["k_cache"].cuda(), d["v_cache"].cuda()
+            seq = d["seqlens_k"].cuda()
+            plan.append_kv(d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, seq)
+            out = plan.decode(d["q"].cuda(), kc, vc, seq, workspace=ws,
+                              head_sink=None if d["head_sink"] is None else d["head_sink"].cuda())
+            _t.cuda.synchronize()
+            compare(out, oracle_decode(w, d), "bf16", f"reuse {rep} {w}")
+
+
+@pytest.mark.parametrize("B,Hkv,curr", [(32, 16, 16), (33, 16, 16)])
+def test_decode_many_row_tiles(gpu, B, Hkv, curr):
+    """Many (batch, KV head, 16-row) tiles in one call: 32*16*4 = 2048 tiles is
+    the most the matrix-core decode takes in one launch; 33*16*4 goes through
+    the one-wave-per-row kernel.  Both must agree with the oracle."""
+    seed = zlib.crc32(repr(("tiles", B, Hkv, curr)).encode())
+    rng = np.random.default_rng(seed)
+    w = Workload("tiles", "decode", "bf16", B=B, Hq=4 * Hkv, Hkv=Hkv, D=64, Lq=curr, Lk=80,
+                 window=24, head_sink=True,
+                 seqlens=("list", rng.integers(curr - 1, 80, size=B).tolist()), seed=seed)
+    d = generate(w)
+    out, _, _ = gpu_decode(w, d)
+    compare(out, oracle_decode(w, d), "bf16", f"decode {w}")

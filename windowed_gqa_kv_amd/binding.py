@@ -211,8 +211,9 @@ class Plan:
         return gqa_workspace_size(self._h)
 
     def new_workspace(self, device="cuda"):
+        """A decode workspace; zero-filled, as the C ABI requires before first use."""
         import torch
-        return torch.empty(max(16, self.workspace_size()), dtype=torch.uint8, device=device)
+        return torch.zeros(max(16, self.workspace_size()), dtype=torch.uint8, device=device)
 
     def _check_dtype(self, *ts):
         want = DTYPE_CODES[self.dtype]

@@ -151,8 +151,7 @@ GQA_API gqa_status gqa_plan(const gqa_attrs* attrs, int32_t max_batch, int32_t m
   p->max_kv_len = max_kv_len;
   p->ws_bytes = 0;
   if (gqa::decode_mfma_supported(a.dtype, a.head_size)) {
-    gqa::DecodeGeometry geo = gqa::decode_geometry(max_batch, a.kv_num_heads, p->G, max_q_len, max_kv_len,
-                                                   a.local_window_size, a.is_causal, a.head_size);
+    gqa::DecodeGeometry geo = gqa::decode_geometry(max_batch, a.kv_num_heads, p->G, max_q_len, a.head_size);
     p->ws_bytes = geo.ws_floats * sizeof(float);
   }
   *out_plan = p;
@@ -266,19 +265,17 @@ GQA_API gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t 
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int dtype = (int)plan->attrs.dtype;
   if (gqa::decode_mfma_supported(dtype, plan->attrs.head_size)) {
-    gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, capacity, a.window, a.causal,
-                                                   a.D);
+    gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
     const size_t need = geo.ws_floats * sizeof(float);
     if (workspace == nullptr || ws_bytes < need)
       return fail(GQA_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
                   workspace ? "" : ", NULL");
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
       return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    if ((int64_t)B * a.Hkv * geo.row_tiles > 65535)
-      return fail(GQA_ERR_UNSUPPORTED, "B * kv_num_heads * row tiles above 65535");
-    return hip_status(gqa::launch_decode_mfma(a, dtype, plan->attrs.softcap > 0, geo,
-                                              reinterpret_cast<float*>(workspace), stream),
-                      "decode launch");
+    if (geo.fits)
+      return hip_status(gqa::launch_decode_mfma(a, dtype, plan->attrs.softcap > 0, geo,
+                                                reinterpret_cast<float*>(workspace), stream),
+                        "decode launch");
   }
   return hip_status(gqa::launch_attn_generic(a, dtype, stream), "decode launch");
 }

@@ -19,19 +19,23 @@ bool prefill_mfma_supported(int dtype, int head_size);
 hipError_t launch_prefill_mfma(const AttnArgs& a, int dtype, bool softcap, hipStream_t stream);
 
 // Split-KV decode on bf16/fp16 MFMA (16x16x32 for QK^T, 16x16x16 for PV):
-// one workgroup per (batch, KV head, 16-row tile, key chunk) writes an
-// fp32 partial (acc, max, sum); a combine kernel merges the partials, folds
-// the sink and writes O.  Head sizes 64, 128, 256.
+// one balanced round of workgroups (as many as the device holds at once)
+// streams equal slices of the flattened list of 16-key units over all
+// (batch, KV head, 16-row tile) row tiles; every piece leaves an fp32
+// partial (acc, max, sum) and the last workgroup of each row tile to finish
+// merges them, folds the sink and writes O.  Head sizes 64, 128, 256.
+// Workspace = per-tile arrival counters (must be zero before the first call;
+// every call leaves them zero) followed by the partials.
 struct DecodeGeometry {
-  int rows;        // G * curr query rows per KV head
-  int row_tiles;   // ceil(rows / 16)
-  int chunk;       // keys per split
-  int splits;      // splits covering the longest possible key range
+  int rows;               // G * curr query rows per KV head
+  int row_tiles;          // ceil(rows / 16)
+  int64_t tiles;          // B * Hkv * row_tiles
+  size_t counter_floats;  // leading workspace words holding the arrival counters
   size_t ws_floats;
+  bool fits;              // tiles within the kernel's per-call limit
 };
 bool decode_mfma_supported(int dtype, int head_size);
-DecodeGeometry decode_geometry(int B, int Hkv, int G, int curr, int64_t capacity,
-                               int window, int causal, int head_size);
+DecodeGeometry decode_geometry(int B, int Hkv, int G, int curr, int head_size);
 hipError_t launch_decode_mfma(const AttnArgs& a, int dtype, bool softcap,
                               const DecodeGeometry& geo, float* ws, hipStream_t stream);
 
