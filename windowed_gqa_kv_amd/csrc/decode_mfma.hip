@@ -26,12 +26,16 @@
 // every workgroup bumps the arrival counter of each tile it touched; the last
 // arrival of a tile merges its partials, folds the sink and writes O.
 //
-// Per 16-key unit: K goes straight from HBM into the A operand of
-// v_mfma_f32_16x16x32 (S^T = K Q^T, Q in registers); V is read with 16-byte
-// coalesced loads, transposed through a wave-private LDS slice and fed to
-// v_mfma_f32_16x16x16 (O^T += V^T P^T), whose B operand layout is exactly the
-// score accumulator layout.  Each wave keeps the next unit's loads in flight
-// while it computes the current one.
+// Per 16-key unit: each wave streams its units into a private ring of LDS
+// stages with wave-wide LDS DMA loads (global_load_lds_dwordx4: 1 KB per
+// instruction, no registers held while in flight), several units ahead of
+// the one it computes.  K rows are read from LDS straight into the A operand
+// of v_mfma_f32_16x16x32 (S^T = K Q^T, Q in registers); V is read with the
+// transposing LDS load ds_read_b64_tr_b16 straight into the A operand of
+// v_mfma_f32_16x16x16 (O^T += V^T P^T), whose B operand layout is exactly
+// the score accumulator layout.  Rows are stored with an XOR swizzle of their
+// 16-byte chunks (chosen per lane in the DMA source address) so that both
+// LDS read patterns are free of bank conflicts.
 #include <algorithm>
 
 #include "kernels.h"
@@ -41,10 +45,100 @@ namespace {
 
 constexpr int kRowsPerTile = 16;
 constexpr int kSub = 16;              // keys per unit (MFMA M)
-constexpr int kVtStride = 24;         // elements per V^T row in LDS (16 keys + pad)
+constexpr int kWaves = 4;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kMaxTiles = 2048;       // row tiles per call on this path
 constexpr int kMaxGrid = 2048;        // workgroups per launch (upper bound)
+
+// LDS staging of one wave: kStages units of K and V, 32 KB in flight.
+template <int D>
+struct Ring {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kSlots = D / 8;                     // 16-byte chunks per key row
+  static constexpr int kUnitBytes = kSub * kRowBytes;      // K (or V) bytes of one unit
+  static constexpr int kDmaPerUnit = kUnitBytes / 1024;    // wave-wide 16-byte DMA loads
+  static constexpr int kStages = 32768 / (2 * kUnitBytes);
+  static constexpr int kWaveBytes = kStages * 2 * kUnitBytes;
+  static_assert(kUnitBytes % 1024 == 0, "a unit is whole DMA instructions");
+  static_assert((kStages - 1) * 2 * kDmaPerUnit <= 63, "vmcnt range");
+};
+
+// Chunk slot of 16-byte chunk cc of key row `key` (0..15) is cc ^ swz(key).
+// The K read (16 rows x one chunk column per 16 lanes) and the transposing V
+// read (4 rows x 2 chunks per 16 lanes) then hit every LDS bank equally.
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (D >= 128)
+    return (2 * key + (key >> 3)) & 15;
+  else
+    return (2 * (key >> 1) + (key >> 3)) & 7;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Wait until at most `pending` units (of M loads each) are still in flight.
+template <int M, int S>
+__device__ __forceinline__ void wait_units(int pending) {
+  if constexpr (S > 1) {
+    if (pending >= S - 1) {
+      wait_vm<(S - 1) * M>();
+      return;
+    }
+    wait_units<M, S - 1>(pending);
+  } else {
+    wait_vm<0>();
+  }
+}
+
+// LDS reads of data that arrived by LDS DMA.  They are written as inline
+// assembly that also waits for its own results: the compiler would otherwise
+// place a wait for every outstanding DMA load (vmcnt(0)) in front of each
+// LDS read, which serialises the stream.  The DMA waits are explicit
+// (wait_units) and precede these blocks.  Their vector results are only ever
+// consumed whole, as MFMA operands: this compiler mis-assigns sub-registers
+// when single elements of a vector-typed inline-asm result are used.
+__device__ __forceinline__ void lds_read2_b128(u32x4& a0, u32x4& a1, uint32_t p0, uint32_t p1) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1)
+      : "v"(p0), "v"(p1)
+      : "memory");
+}
+__device__ __forceinline__ void lds_read4_tr16(u32x2& a0, u32x2& a1, u32x2& a2, u32x2& a3, uint32_t p0,
+                                               uint32_t p1, uint32_t p2, uint32_t p3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(p * M) for a wave-uniform p in [0, P].
+template <int M, int P>
+__device__ __forceinline__ void wait_vm_multiple(int p) {
+  if constexpr (P > 0) {
+    if (p >= P) {
+      wait_vm<P * M>();
+      return;
+    }
+    wait_vm_multiple<M, P - 1>(p);
+  } else {
+    wait_vm<0>();
+  }
+}
 
 template <bool IS_BF16>
 __device__ __forceinline__ f32x4 mma_qk(u32x4 a, u32x4 b, f32x4 c) {
@@ -65,11 +159,6 @@ __device__ __forceinline__ f32x4 mma_pv(u32x2 a, u32x2 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Partials travel between workgroups (possibly on different XCDs, whose L2s
 // are not coherent with each other): writers use device-scope relaxed atomic
@@ -118,22 +207,23 @@ __device__ __forceinline__ void store_row4(const AttnArgs& a, int b, int h, int 
 template <bool IS_BF16, int D, bool SOFTCAP>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int nrt,
                                                      float* __restrict__ part, unsigned* __restrict__ counters) {
+  using RG = Ring<D>;
   constexpr int KQ = D / 32;    // k-steps of 16x16x32 over the head dim
   constexpr int DB = D / 16;    // 16-wide output blocks
-  constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int KPL = D / 32;   // keys per lane in the V transpose
+  constexpr int S = RG::kStages;
   constexpr int PART = kRowsPerTile * D + 2 * kRowsPerTile;  // floats per partial
   constexpr int MERGE = D / 4 + 2;                            // floats per lane in a merge slot
   constexpr int XB = 64;                                      // partials per combine batch
-  // V^T slices of the 4 waves; between pieces the same bytes hold the merge
-  // slots, and in the combine the per-split maxima and sums.
-  static_assert(2 * MERGE * 64 * 4 <= 4 * D * kVtStride * 2, "merge slots fit the V^T slices");
-  static_assert(2 * XB * kRowsPerTile + 3 * kRowsPerTile <= 4 * D * kVtStride / 2, "combine fits LDS");
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[4][D * kVtStride];
+  // The rings hold the LDS stages while streaming, the wave merge slots
+  // between pieces and the combine's per-split maxima and sums at the end.
+  static_assert(2 * MERGE * 64 * 4 <= kWaves * RG::kWaveBytes, "merge slots fit the rings");
+  static_assert((2 * XB * kRowsPerTile + 4 * kRowsPerTile) * 4 <= kWaves * RG::kWaveBytes, "combine fits");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kWaves * RG::kWaveBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds[kRowsPerTile * 2 * D];  // Q tile, swizzled like K
   __shared__ int pre[kMaxTiles + 1];  // unit prefix sum over tiles
   __shared__ int wsum[4];
-  __shared__ int flag;
-  float (*merge_lds)[MERGE * 64] = reinterpret_cast<float (*)[MERGE * 64]>(&vt_lds[0][0]);
+  __shared__ int flag[256];
+  float (*merge_lds)[MERGE * 64] = reinterpret_cast<float (*)[MERGE * 64]>(&ring[0]);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,8 +289,22 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   int t_last = t_first - 1;  // last tile this workgroup touches
 
   const float c_l2 = SOFTCAP ? 1.0f : a.scale_log2;
-  uint16_t* vt = vt_lds[w];
-  const int vdc = lane % CPR, vkg = lane / CPR;
+  unsigned char* const my_ring = ring + w * RG::kWaveBytes;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)(lds_void*)my_ring;  // LDS byte address
+  const uint32_t q_addr = (uint32_t)(uintptr_t)(lds_void*)q_lds;
+  // Per-lane LDS read offsets, the same for every unit.  K (and Q) operand:
+  // row n, chunk 4 ks + q4.  V^T operand (transposing read): rows
+  // 4 q4 + (n >> 2), columns 16 db + 4 (n & 3) .. + 3.
+  uint32_t k_off[KQ], v_off[DB];
+#pragma unroll
+  for (int ks = 0; ks < KQ; ++ks) k_off[ks] = n * RG::kRowBytes + 16 * ((4 * ks + q4) ^ swz<D>(n));
+  {
+    const int v_key = 4 * q4 + (n >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      v_off[db] = RG::kUnitBytes + v_key * RG::kRowBytes + 16 * ((2 * db + ((n >> 1) & 1)) ^ swz<D>(v_key)) +
+                  8 * (n & 1);
+  }
 
   // ---- stream the slice, one piece (slice x tile) at a time ----
   int u = ustart;
@@ -229,71 +333,70 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + x.b * a.k_sb + x.g * a.k_sh;
     const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + x.b * a.v_sb + x.g * a.v_sh;
 
+    // Q tile -> LDS by DMA, shared by the 4 waves (instruction i by wave i % 4).
+    // Padding rows load the tile's last real row (in bounds, finite); MFMA
+    // columns are independent, so they only produce unused output rows.
+    constexpr int QDMA = kRowsPerTile * 2 * D / 1024;
+#pragma unroll
+    for (int i = 0; i < QDMA; ++i) {
+      if (i % kWaves != w) continue;
+      const int pos = 64 * i + lane;
+      const int r = pos / RG::kSlots;
+      const int cc = (pos % RG::kSlots) ^ swz<D>(r);
+      const int qr = kRowsPerTile * x.rt + min(r, x.rows_tile - 1);
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(a.q) + x.b * a.q_sb +
+                            (x.g * a.G + qr % a.G) * a.q_sh + (int64_t)(qr / a.G) * a.q_ss + 8 * cc;
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(q_lds + 1024 * i), 16, 0, 0);
+    }
+
     // units of this wave: ua + w, ua + w + 4, ...
     const int nw = ub - ua > w ? (ub - ua - w + 3) / 4 : 0;
-    // Loads are unconditional: a row past the piece end is clamped to the
-    // piece's last key (a real key, finite, masked out for every query row),
-    // so there is no per-lane branch and the wait counters keep the next
-    // unit's loads in flight while the current one is computed.
-    u32x4 kr[2][KQ], vr[2][KPL];
-    auto issue = [&](int slot, int j) {
+    // Rows past the piece end are clamped to its last key (a real key,
+    // finite, masked out for every query row): no per-lane branches.
+    auto issue = [&](int s, int j) {
       const int kb = c_lo + kSub * (w + 4 * j);
-      const int jk = min(kb + n, c_hi);
+      unsigned char* kdst = my_ring + s * 2 * RG::kUnitBytes;
+      unsigned char* vdst = kdst + RG::kUnitBytes;
 #pragma unroll
-      for (int ks = 0; ks < KQ; ++ks)
-        kr[slot][ks] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)jk * a.k_ss + 32 * ks + 8 * q4);
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        const int jv = min(kb + vkg * KPL + e, c_hi);
-        vr[slot][e] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)jv * a.v_ss + 8 * vdc);
+      for (int i = 0; i < RG::kDmaPerUnit; ++i) {
+        const int pos = 64 * i + lane;                 // 16-byte chunk position in the unit
+        const int key = pos / RG::kSlots;
+        const int cc = (pos % RG::kSlots) ^ swz<D>(key);  // the global chunk stored there
+        const int row = min(kb + key, c_hi);
+        __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)row * a.k_ss + 8 * cc),
+                                         (lds_void*)(kdst + 1024 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)row * a.v_ss + 8 * cc),
+                                         (lds_void*)(vdst + 1024 * i), 16, 0, 0);
       }
     };
-    if (nw > 0) issue(0, 0);
+    const int npro = min(nw, S);
+    for (int j = 0; j < npro; ++j) issue(j, j);
+    // Q landed once only the prologue units are younger; then every wave's
+    // part is in LDS after the barrier (no fence: nothing else to order).
+    wait_vm_multiple<2 * RG::kDmaPerUnit, S>(npro);
+    __builtin_amdgcn_s_barrier();
     u32x4 qf[KQ];
-    {
-      // padding rows load a row of the group (in bounds) and are zeroed
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + x.b * a.q_sb + my_h * a.q_sh +
-                           (int64_t)my_t * a.q_ss + 8 * q4;
 #pragma unroll
-      for (int ks = 0; ks < KQ; ++ks) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        qf[ks] = row_ok ? v : z;
-      }
-    }
+    for (int ks = 0; ks < KQ; ks += 2)
+      lds_read2_b128(qf[ks], qf[ks + 1], q_addr + k_off[ks], q_addr + k_off[ks + 1]);
 
     f32x4 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4{};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    auto compute = [&](int slot, int j) {
+    for (int j = 0; j < nw; ++j) {
+      const int s = j % S;
+      wait_units<2 * RG::kDmaPerUnit, S>(min(S - 1, nw - 1 - j));
       const int kb = c_lo + kSub * (w + 4 * j);
-      // V -> V^T in this wave's LDS slice (reads of the previous unit are
-      // issued before these writes in program order)
-      wave_lds_fence();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * vdc + e;
-        uint16_t* dst = vt + d * kVtStride + vkg * KPL;
-        uint32_t pk[KPL / 2];
-#pragma unroll
-        for (int y = 0; y < KPL / 2; ++y) {
-          const uint32_t x0 = vr[slot][2 * y][e >> 1], x1 = vr[slot][2 * y + 1][e >> 1];
-          pk[y] = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-        }
-        if constexpr (KPL == 8) {
-          *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        } else if constexpr (KPL == 4) {
-          *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = pk[0];
-        }
-      }
+      const uint32_t st = ring_addr + s * 2 * RG::kUnitBytes;
       // S^T = K Q^T
+      u32x4 kf[KQ];
+#pragma unroll
+      for (int ks = 0; ks < KQ; ks += 2) lds_read2_b128(kf[ks], kf[ks + 1], st + k_off[ks], st + k_off[ks + 1]);
       f32x4 sc = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < KQ; ++ks) sc = mma_qk<IS_BF16>(kr[slot][ks], qf[ks], sc);
+      for (int ks = 0; ks < KQ; ++ks) sc = mma_qk<IS_BF16>(kf[ks], qf[ks], sc);
       if constexpr (SOFTCAP) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = a.cap_log2 * tanh_f32(sc[r] * a.scale_over_cap);
@@ -330,22 +433,16 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
         l_run += pv[r];
       }
       const u32x2 pp = u32x2{pack2<IS_BF16>(pv[0], pv[1]), pack2<IS_BF16>(pv[2], pv[3])};
-      // O^T += V^T P^T
-      wave_lds_fence();
+      // O^T += V^T P^T, V^T read transposed out of the row-major stage
+      u32x2 vf[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2 vf = *reinterpret_cast<const u32x2*>(vt + (16 * db + n) * kVtStride + 4 * q4);
-        o[db] = mma_pv<IS_BF16>(vf, pp, o[db]);
-      }
-    };
-
-    // two-slot pipeline: the next unit's loads go out before this unit's math
-    for (int j = 0; j < nw; j += 2) {
-      if (j + 1 < nw) issue(1, j + 1);
-      compute(0, j);
-      if (j + 1 >= nw) break;
-      if (j + 2 < nw) issue(0, j + 2);
-      compute(1, j + 1);
+      for (int db = 0; db < DB; db += 4)
+        lds_read4_tr16(vf[db], vf[db + 1], vf[db + 2], vf[db + 3], st + v_off[db], st + v_off[db + 1],
+                       st + v_off[db + 2], st + v_off[db + 3]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = mma_pv<IS_BF16>(vf[db], pp, o[db]);
+      // refill this stage (its LDS reads are consumed above)
+      if (j + S < nw) issue(s, j + S);
     }
 
     // ---- merge the 4 waves through LDS (lane-to-lane: identical layouts) ----
@@ -396,7 +493,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
         }
       }
     }
-    __syncthreads();  // the merge slots are V^T slices again for the next piece
+    __syncthreads();  // the merge slots are ring stages again for the next piece
     ++t;
   }
 
@@ -405,24 +502,32 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  float* lf = reinterpret_cast<float*>(&vt_lds[0][0]);  // [XB][16] maxima, then factors
+  float* lf = reinterpret_cast<float*>(&ring[0]);  // [XB][16] maxima, then factors
   float* ls = lf + XB * kRowsPerTile;                     // [XB][16] sums
   float* rowM = ls + XB * kRowsPerTile;
   float* rowL = rowM + kRowsPerTile;
   float* rowA = rowL + kRowsPerTile;
+  float* rowS = rowA + kRowsPerTile;
   bool acquired = false;
-  for (int tt = t_first; tt <= t_last; ++tt) {
-    if (pre[tt + 1] == pre[tt]) continue;
+  for (int base = t_first; base <= t_last; base += 256) {
+  // one arrival per touched tile, all in flight together
+  const int nbt = min(256, t_last - base + 1);
+  if (tid < nbt) {
+    const int tt = base + tid;
+    int f = 0;
+    if (pre[tt + 1] != pre[tt]) {
+      const int nvalid = owner_of(pre[tt + 1] - 1, U, Gs) - owner_of(pre[tt], U, Gs) + 1;
+      f = __hip_atomic_fetch_add(&counters[tt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          (unsigned)(nvalid - 1);
+    }
+    flag[tid] = f;
+  }
+  __syncthreads();
+  for (int i = 0; i < nbt; ++i) {
+    if (!flag[i]) continue;
+    const int tt = base + i;
     const int first = owner_of(pre[tt], U, Gs);
-    const int last = owner_of(pre[tt + 1] - 1, U, Gs);
-    const int nvalid = last - first + 1;
-    if (tid == 0)
-      flag = __hip_atomic_fetch_add(&counters[tt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(nvalid - 1);
-    __syncthreads();
-    const bool is_last = flag;
-    __syncthreads();
-    if (!is_last) continue;
+    const int nvalid = owner_of(pre[tt + 1] - 1, U, Gs) - first + 1;
     if (!acquired) {
       // acquire at device scope once: the plain loads below then see the
       // other workgroups' write-through stores
@@ -432,17 +537,37 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     const Tile x = make_tile(a, rows, nrt, tt);
     const float* gpart = part + (int64_t)(first + tt) * PART;
 
-    // Merge the nvalid partials, XB at a time.  Per batch: (1) every (split,
-    // row) max and sum is fetched in parallel into LDS; (2) one thread per row
-    // moves the row's running max, rescales its running sum and turns the
-    // batch's maxima into factors exp2(m_x - M); (3) TQ threads per output
-    // quad accumulate factor * acc over disjoint splits (all relative to the
-    // same M), reduced with shuffles at the end.
+    // Merge the nvalid partials in batches.  Per batch: (1) every thread
+    // issues the loads of all its partial accumulators of the batch (output
+    // quads x splits, clamped indices, all in flight together), then (2) the
+    // per-(split, row) maxima and sums are fetched into LDS -- one round trip
+    // for both; (3) one thread per row moves the row's running max, rescales
+    // its running sum and turns the batch's maxima into factors exp2(m_x - M);
+    // (4) TQ threads per output quad accumulate factor * acc over disjoint
+    // splits (all relative to the same M), reduced with shuffles at the end.
     const int items = x.rows_tile * (D / 4);
     // threads per output quad: the largest power of two with items * TQ <= 256
     const int TQ = items <= 16 ? 16 : (items <= 32 ? 8 : (items <= 64 ? 4 : (items <= 128 ? 2 : 1)));
     const int t_sub = tid % TQ;
     constexpr int IPT = (kRowsPerTile * (D / 4) + 255) / 256;  // output quads per thread when TQ == 1
+    constexpr int NPT = 32 / IPT;                               // splits per output quad and batch
+    const int XBt = min(XB, NPT * TQ);
+    int it_r[IPT], it_d[IPT];
+    bool it_ok[IPT];
+#pragma unroll
+    for (int q = 0; q < IPT; ++q) {
+      const int item = (tid / TQ) + q * (256 / TQ);
+      it_ok[q] = item < items;
+      const int ic = it_ok[q] ? item : 0;
+      it_r[q] = ic / (D / 4);
+      it_d[q] = ic % (D / 4);
+    }
+    // sink logits of the tile's rows, fetched now so that the load overlaps the partials'
+    float sink_row = 0.0f;
+    if (a.use_sink && tid < x.rows_tile) {
+      const int row = kRowsPerTile * x.rt + tid;
+      sink_row = sink_log2(a, x.g * a.G + row % a.G);
+    }
     f32x4 acc[IPT];
 #pragma unroll
     for (int q = 0; q < IPT; ++q) acc[q] = f32x4{};
@@ -450,9 +575,21 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       rowM[tid] = -INFINITY;
       rowL[tid] = 0.0f;
     }
-    for (int xb = 0; xb < nvalid; xb += XB) {
-      const int nb = min(XB, nvalid - xb);
-      __syncthreads();
+    for (int xb = 0; xb < nvalid; xb += XBt) {
+      const int nb = min(XBt, nvalid - xb);
+      f32x4 v[IPT][NPT];
+#pragma unroll
+      for (int q = 0; q < IPT; ++q)
+#pragma unroll
+        for (int e = 0; e < NPT; ++e) {
+          const int xs = min(t_sub + e * TQ, nb - 1);
+          v[q][e] = *reinterpret_cast<const f32x4*>(gpart + (int64_t)(xb + xs) * PART + it_r[q] * D + 4 * it_d[q]);
+        }
+      // the previous batch's factor reads are complete before they are
+      // overwritten (LDS-only fences: no DMA load is in flight here)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       for (int pr = tid; pr < nb * x.rows_tile; pr += 256) {
         const int xs = pr / x.rows_tile, r = pr % x.rows_tile;
         const float* p = gpart + (int64_t)(xb + xs) * PART + kRowsPerTile * D;
@@ -485,26 +622,25 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < IPT; ++q) {
-        const int item = (tid / TQ) + q * (256 / TQ);
-        if (item >= items) break;
-        const int r = item / (D / 4), dq = item % (D / 4);
+        if (!it_ok[q]) continue;
+        const int r = it_r[q];
         acc[q] *= rowA[r];
-#pragma unroll 8
-        for (int xs = t_sub; xs < nb; xs += TQ) {
-          const float* p = gpart + (int64_t)(xb + xs) * PART + r * D + 4 * dq;
-          acc[q] += *reinterpret_cast<const f32x4*>(p) * lf[xs * kRowsPerTile + r];
+#pragma unroll
+        for (int e = 0; e < NPT; ++e) {
+          const int xs = t_sub + e * TQ;
+          acc[q] += v[q][e] * (xs < nb ? lf[xs * kRowsPerTile + r] : 0.0f);
         }
       }
     }
+    if (tid < x.rows_tile) rowS[tid] = sink_row;
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < IPT; ++q) {
       for (int off = TQ / 2; off > 0; off >>= 1)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[q][e] += __shfl_xor(acc[q][e], off, 64);
-      const int item = (tid / TQ) + q * (256 / TQ);
-      if (item >= items || t_sub != 0) continue;
-      const int r = item / (D / 4), dq = item % (D / 4);
+      if (!it_ok[q] || t_sub != 0) continue;
+      const int r = it_r[q], dq = it_d[q];
       const int row = kRowsPerTile * x.rt + r;
       const int h = x.g * a.G + row % a.G;
       const float M = rowM[r], L = rowL[r];
@@ -512,7 +648,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       if (M == -INFINITY) {
         fac = 0.0f;
       } else if (a.use_sink) {
-        const float tsk = sink_log2(a, h);
+        const float tsk = rowS[r];
         const float M2 = fmaxf(M, tsk);
         const float e1 = fast_exp2(M - M2);
         fac = e1 / (L * e1 + fast_exp2(tsk - M2));
@@ -524,6 +660,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     if (tid == 0)  // ready for the next call
       __hip_atomic_store(&counters[tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
+  }
+  __syncthreads();  // flag[] is rewritten by the next batch of tiles
   }
 }
 
