@@ -24,7 +24,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -48,15 +47,22 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
+                    help="only run 10 plain device copies of MIB MiB (the reference kernel that "
+                         "scales the FETCH_SIZE/WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
-def _src_hash(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "windowed_gqa_kv_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def copy_calibration(mib: float):
+    """10 device-to-device copies of a known size, for counter calibration."""
+    import torch
+    n = int(mib * (1 << 20))
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(10):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "copies": 10}), flush=True)
 
 
 def _traffic(kernel: str, workload: str, src_files):
@@ -68,8 +74,9 @@ def _traffic(kernel: str, workload: str, src_files):
             table = json.load(f)
     except (OSError, ValueError):
         return None
+    from windowed_gqa_kv_amd.profiling import src_hash
     rec = table.get(f"{kernel}/{workload}")
-    if not rec or rec.get("src_hash") != _src_hash(src_files):
+    if not rec or rec.get("src_hash") != src_hash(src_files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -200,6 +207,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     binding.load()
     byname = {w.name: w for w in WORKLOADS.values()}
     w = byname[args.workload]
