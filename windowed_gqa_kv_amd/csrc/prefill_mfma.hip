@@ -12,18 +12,26 @@
 //
 // Layout of the work.
 //   * Workgroup = 4 waves = 128 query rows of one (batch, query head); wave w
-//     owns rows [32w, 32w+32).  Key tiles of 64 rows are staged in LDS (double
-//     buffered, one barrier per tile) and shared by the 4 waves.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K tile from LDS, B = Q held in
+//     owns rows [32w, 32w+32).  Key tiles of 64 rows of K and of V are copied
+//     from global memory straight into LDS by LDS DMA (global_load_lds_dwordx4,
+//     no registers held by loads in flight), double buffered, one barrier per
+//     tile; the 4 waves share them.  Two workgroups fit on a CU.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q held in
 //     registers for the whole kernel), so each lane ends up owning one query
 //     row and 16 keys of every 32-key sub-tile.  The K rows fed to the MFMA M
 //     index are permuted (key_of_m) so that those 16 keys come as two runs of
 //     8 consecutive keys -- exactly the B-operand layout the P*V MFMA needs.
 //     P therefore goes from the score accumulators to the next MFMA without
 //     an LDS round trip.
-//   * O^T += V^T P^T on the same MFMA: V is transposed once while it is
-//     written to LDS (4 keys x 8 dims per thread, 8-byte writes), so every
-//     MFMA operand is a single 16-byte LDS read.
+//   * O^T += V^T P^T on the same MFMA: the A operand (8 consecutive keys of one
+//     head-dim column per lane) comes out of the row-major V tile through two
+//     transposing LDS reads (ds_read_b64_tr_b16).  K and V rows are stored with
+//     XOR-swizzled 16-byte chunks (chosen per lane in the DMA source address),
+//     which keeps both read patterns free of bank conflicts.
+//   * Operand reads are batched (four K operands, or the four V operands of one
+//     16-key step, per wait) and consecutive MFMAs update different
+//     accumulators; tiles fully inside every row's band take a branch-free
+//     path.
 //   * Online softmax in fp32 with exp2, the scale folded into one FMA, a lazy
 //     rescale (the running max only moves when it grows by more than 2^8),
 //     and masks evaluated only on boundary sub-tiles; sub-tiles a wave cannot
@@ -31,6 +39,8 @@
 //   * Work items are ordered (batch, KV head)-major so that the query heads
 //     sharing one K/V land on the same XCD (its own L2), heaviest row blocks
 //     first within each KV head.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gqa {
@@ -57,18 +67,106 @@ __device__ __forceinline__ int key_of_m(int m) {
   const int a = m >> 3, hh = (m >> 2) & 1, c = m & 3;
   return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + c;
 }
-// XOR swizzles of 16-byte chunks (bank-conflict-free 16-byte LDS reads).
+// XOR swizzle of the 16-byte chunks of K row r (conflict-free operand reads).
 __device__ __forceinline__ int k_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
-__device__ __forceinline__ int v_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+// V tile rows (row-major, 16-byte chunks XOR-swizzled by key): the
+// transposing reads of the P*V operand then hit every bank equally.
+template <int D>
+__device__ __forceinline__ int vrow_swz(int key) {
+  if constexpr (D == 128)
+    return 4 * (key & 3);
+  else
+    return 4 * ((key >> 1) & 1);
+}
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+// LDS reads of DMA-filled tiles are inline assembly: the compiler would put a
+// wait for every LDS DMA load in flight (the next tile's) in front of each
+// of them.  Results are consumed whole, as MFMA operands (single elements of
+// a vector-typed inline-asm result are mis-assigned to sub-registers by this
+// compiler); the 64-bit halves of a V operand come back as scalars.
+__device__ __forceinline__ u32x4 lds_b128(uint32_t p) {
+  u32x4 v;
+  asm volatile(
+      "ds_read_b128 %0, %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(v)
+      : "v"(p)
+      : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x4 lds_tr16x2(uint32_t p0, uint32_t p1) {
+  uint64_t a, b;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b)
+      : "v"(p0), "v"(p1)
+      : "memory");
+  return __builtin_bit_cast(u32x4, u64x2{a, b});
+}
+__device__ __forceinline__ void lds_b128x4(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, uint32_t p0,
+                                           uint32_t p1, uint32_t p2, uint32_t p3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+      : "memory");
+}
+__device__ __forceinline__ void lds_b128x2(u32x4& a0, u32x4& a1, uint32_t p0, uint32_t p1) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1)
+      : "v"(p0), "v"(p1)
+      : "memory");
+}
+// Four P*V operands (8 transposing reads), one wait.
+__device__ __forceinline__ void lds_tr16x8(u32x4 (&v)[4], const uint32_t (&p)[8]) {
+  uint64_t r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+      : "memory");
+  v[0] = __builtin_bit_cast(u32x4, u64x2{r0, r1});
+  v[1] = __builtin_bit_cast(u32x4, u64x2{r2, r3});
+  v[2] = __builtin_bit_cast(u32x4, u64x2{r4, r5});
+  v[3] = __builtin_bit_cast(u32x4, u64x2{r6, r7});
+}
+// Barrier for waves whose only LDS accesses are the inline-assembly ones:
+// wait for this wave's LDS operations, then meet.  (A fenced barrier would
+// also wait for the next tile's DMA loads, which count as LDS writes.)
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Two waves per SIMD (two workgroups per CU): the register budget is 256.
 template <bool IS_BF16, int D, bool SOFTCAP>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int nrb, int items,
-                                                           int per_xcd) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
+    AttnArgs a, int nrb, int items, int per_xcd) {
   constexpr int KS = D / 16;    // k-steps of the QK^T contraction
   constexpr int DB = D / 32;    // 32-wide output blocks
   constexpr int CPR = D / 8;    // 16-byte chunks per K row
-  constexpr int KPT = D / 32;   // keys per thread in the V transpose (and K chunks per thread)
-  constexpr int TILE = BN * D;  // elements of one K (or V^T) tile
+  constexpr int TILE = BN * D;  // elements of one K (or V) tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * TILE];
 
   // ---- work item: XCD-major, KV-head-major, heavy row blocks first ----
@@ -131,170 +229,185 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(AttnArgs a, int nrb, 
 
   const int nblk = kv_lo <= kv_hi ? (kv_hi - kv_lo + BN) / BN : 0;
 
-  u32x4 kst[KPT], vst[KPT];
-  // Global -> registers for the tile starting at key kb.  Keys past kv_hi
-  // are never read; zeros stand in for them.
-  auto gload = [&](int kb) {
+  // K and V tiles go from global memory straight into LDS (LDS DMA, 1 KB per
+  // wave-wide instruction).  Both are row-major with XOR-swizzled 16-byte
+  // chunks; lane L of instruction i writes position 64 i + L, so it loads the
+  // global chunk that the swizzle puts there.  Rows past kv_hi are clamped to
+  // kv_hi: real, finite keys that the masks remove for every row.
+  constexpr int NDMA = TILE * 2 / 1024 / 4;  // per wave, per tile, per tensor
+  auto dma_tile = [&](int kb, int buf) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CPR, cc = c % CPR;
-      const int j = kb + r;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kst[i] = j <= kv_hi ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)j * a.k_ss + 8 * cc) : z;
-    }
-    const int dc = tid % CPR, kg = tid / CPR;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int j = kb + kg * KPT + i;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      vst[i] = j <= kv_hi ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)j * a.v_ss + 8 * dc) : z;
-    }
-  };
-  // Registers -> LDS: K row-major (swizzled), V transposed to [D][BN] (swizzled).
-  auto lstore = [&](int buf) {
-    uint16_t* Ks = lds[buf];
-    uint16_t* Vt = lds[buf] + TILE;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CPR, cc = c % CPR;
-      *reinterpret_cast<u32x4*>(Ks + r * D + 8 * (cc ^ k_swz(r))) = kst[i];
-    }
-    const int dc = tid % CPR, kg = tid / CPR;
-    const int key0 = kg * KPT;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * dc + e;
-      const int chunk = key0 >> 3;
-      uint16_t* dst = Vt + d * BN + 8 * (chunk ^ v_swz(d)) + (key0 & 7);
-      if constexpr (KPT == 4) {
-        const uint32_t x0 = vst[0][e >> 1], x1 = vst[1][e >> 1];
-        const uint32_t x2 = vst[2][e >> 1], x3 = vst[3][e >> 1];
-        u32x2 pk;
-        if (e & 1) {
-          pk[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-          pk[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-        } else {
-          pk[0] = (x0 & 0xffffu) | (x1 << 16);
-          pk[1] = (x2 & 0xffffu) | (x3 << 16);
-        }
-        *reinterpret_cast<u32x2*>(dst) = pk;
-      } else {
-        static_assert(KPT == 2, "head size 64 or 128");
-        const uint32_t x0 = vst[0][e >> 1], x1 = vst[1][e >> 1];
-        const uint32_t pk = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-        *reinterpret_cast<uint32_t*>(dst) = pk;
-      }
+    for (int i = 0; i < NDMA; ++i) {
+      const int ii = NDMA * w + i;  // instruction index within the tile
+      const int pos = 64 * ii + lane;
+      const int r = pos / CPR, slot = pos % CPR;
+      const int j = min(kb + r, kv_hi);
+      const int ck = slot ^ k_swz(r);
+      const int cv = slot ^ vrow_swz<D>(r);
+      __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)j * a.k_ss + 8 * ck),
+                                       (lds_void*)(&lds[buf][0] + 512 * ii), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)j * a.v_ss + 8 * cv),
+                                       (lds_void*)(&lds[buf][TILE] + 512 * ii), 16, 0, 0);
     }
   };
 
   const float c_l2 = SOFTCAP ? 1.0f : a.scale_log2;  // raw units -> log2 units
   const int kr0 = key_of_m(n);                        // this lane's K row in a sub-tile
 
-  if (nblk > 0) {
-    gload(kv_lo);
-    lstore(0);
-  }
-  __syncthreads();
+  if (nblk > 0) dma_tile(kv_lo, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // Q registers and the first tile
+  tile_barrier();
 
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0];
+  // per-lane byte offsets of the transposing V reads: rows 8 (g >> 1) + 4 r + j
+  // of each 16-key group, columns 16 (g & 1) + 4 c .. + 3 of each 32-column block
+  const int tg = lane >> 4, tj = (lane >> 2) & 3, tc = lane & 3;
   for (int it = 0; it < nblk; ++it) {
     const int kb = kv_lo + it * BN;
     const int buf = it & 1;
-    if (it + 1 < nblk) gload(kb + BN);
+    if (it + 1 < nblk) dma_tile(kb + BN, buf ^ 1);
 
-    const uint16_t* Ks = lds[buf];
-    const uint16_t* Vt = lds[buf] + TILE;
-    // Scores of the two 32-key sub-tiles.  A sub-tile this wave cannot see is
-    // skipped and its accumulator is never read (every consumer below tests
-    // act[]); no register fill stands in for it.
-    bool act[2];
-    f32x16 s[2];
-    float bm = -INFINITY;
+    // Sub-tiles (32 keys) this wave can see.  Interior tiles take the
+    // branch-free path (both active), so that LDS reads can be scheduled
+    // ahead of the MFMAs; frontier tiles take the general one.
+    const bool act0 = wrows > 0 && kb <= w_hi && kb + 31 >= w_lo;
+    const bool act1 = wrows > 0 && kb + 32 <= w_hi && kb + 63 >= w_lo;
+    auto tile = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      const bool act[2] = {FULL || act0, FULL || act1};
+      // ---- S^T = K Q^T for both sub-tiles, the two chains interleaved ----
+      f32x16 s[2];
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+      const uint32_t kbase = lds0 + buf * (2 * TILE * 2);
+      const uint32_t kp0 = kbase + 2 * kr0 * D;
+      const uint32_t kp1 = kbase + 2 * (32 + kr0) * D;
+      const int sw0 = k_swz(kr0), sw1 = k_swz(32 + kr0);
+      if constexpr (FULL) {
+        // both sub-tiles, two k-steps per batch of LDS reads
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int k0 = kb + 32 * sub;
-      act[sub] = wrows > 0 && k0 <= w_hi && k0 + 31 >= w_lo;
-      if (!act[sub]) continue;
-      const int r = 32 * sub + kr0;
-      const uint16_t* kp = Ks + r * D;
-      const int sw = k_swz(r);
-      f32x16 acc = f32x16{};
+        for (int ks = 0; ks < KS; ks += 2) {
+          u32x4 k00, k10, k01, k11;
+          lds_b128x4(k00, k10, k01, k11, kp0 + 16 * ((2 * ks + h2) ^ sw0), kp1 + 16 * ((2 * ks + h2) ^ sw1),
+                     kp0 + 16 * ((2 * ks + 2 + h2) ^ sw0), kp1 + 16 * ((2 * ks + 2 + h2) ^ sw1));
+          s[0] = mma32<IS_BF16>(k00, qf[ks], s[0]);
+          s[1] = mma32<IS_BF16>(k10, qf[ks], s[1]);
+          s[0] = mma32<IS_BF16>(k01, qf[ks + 1], s[0]);
+          s[1] = mma32<IS_BF16>(k11, qf[ks + 1], s[1]);
+        }
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kp + 8 * ((2 * ks + h2) ^ sw));
-        acc = mma32<IS_BF16>(kf, qf[ks], acc);
-      }
-      if constexpr (SOFTCAP) {
+        for (int sub = 0; sub < 2; ++sub) {
+          if (!act[sub]) continue;
+          const uint32_t kp = sub ? kp1 : kp0;
+          const int sw = sub ? sw1 : sw0;
 #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) acc[r2] = a.cap_log2 * tanh_f32(acc[r2] * a.scale_over_cap);
-      }
-      // masks only where the sub-tile crosses a frontier of some row of this wave
-      const bool interior = (a.window < 0 || k0 >= pw1 - a.window + 1) &&
-                            (!a.causal || k0 + 31 <= pw0) && (k0 + 31 < sp.valid);
-      if (!interior) {
-#pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) {
-          const int j = k0 + 16 * (r2 >> 3) + 8 * h2 + (r2 & 7);
-          acc[r2] = (j < my_lo || j > my_hi) ? -INFINITY : acc[r2];
+          for (int ks = 0; ks < KS; ks += 2) {
+            u32x4 ka, kb2;
+            lds_b128x2(ka, kb2, kp + 16 * ((2 * ks + h2) ^ sw), kp + 16 * ((2 * ks + 2 + h2) ^ sw));
+            s[sub] = mma32<IS_BF16>(ka, qf[ks], s[sub]);
+            s[sub] = mma32<IS_BF16>(kb2, qf[ks + 1], s[sub]);
+          }
         }
       }
+      float bm = -INFINITY;
 #pragma unroll
-      for (int r2 = 0; r2 < 16; ++r2) bm = fmaxf(bm, acc[r2]);
-      s[sub] = acc;
-    }
-
-    // ---- online softmax (lane owns row n; lanes n and n+32 share the row) ----
-    bm = fmaxf(bm, xor32(bm));
-    const float m_new = fmaxf(m_run, bm);
-    const bool need = (m_new - m_run) * c_l2 > kRescaleLog2;  // false while both are -inf
-    if (__any(need)) {
-      const float alpha = need ? fast_exp2((m_run - m_new) * c_l2) : 1.0f;
-      m_run = need ? m_new : m_run;
-      l_run *= alpha;
+      for (int sub = 0; sub < 2; ++sub) {
+        if (!act[sub]) continue;
+        const int k0 = kb + 32 * sub;
+        f32x16& acc = s[sub];
+        if constexpr (SOFTCAP) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+          for (int r2 = 0; r2 < 16; ++r2) acc[r2] = a.cap_log2 * tanh_f32(acc[r2] * a.scale_over_cap);
+        }
+        // masks only where the sub-tile crosses a frontier of some row of this wave
+        const bool interior = (a.window < 0 || k0 >= pw1 - a.window + 1) &&
+                              (!a.causal || k0 + 31 <= pw0) && (k0 + 31 < sp.valid);
+        if (!interior) {
 #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) o[db][r2] *= alpha;
-    }
-    const float mb = m_run == -INFINITY ? 0.0f : m_run * c_l2;
-    u32x4 pb[2][2];
+          for (int r2 = 0; r2 < 16; ++r2) {
+            const int j = k0 + 16 * (r2 >> 3) + 8 * h2 + (r2 & 7);
+            acc[r2] = (j < my_lo || j > my_hi) ? -INFINITY : acc[r2];
+          }
+        }
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (!act[sub]) continue;
-      float pv[16];
-#pragma unroll
-      for (int r2 = 0; r2 < 16; ++r2) {
-        pv[r2] = fast_exp2(fmaf(s[sub][r2], c_l2, -mb));
-        l_run += pv[r2];
+        for (int r2 = 0; r2 < 16; ++r2) bm = fmaxf(bm, acc[r2]);
       }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2)
-          pb[sub][t][q2] = pack2<IS_BF16>(pv[8 * t + 2 * q2], pv[8 * t + 2 * q2 + 1]);
-    }
 
-    // ---- O^T += V^T P^T ----
+      // ---- online softmax (lane owns row n; lanes n and n+32 share the row) ----
+      bm = fmaxf(bm, xor32(bm));
+      const float m_new = fmaxf(m_run, bm);
+      const bool need = (m_new - m_run) * c_l2 > kRescaleLog2;  // false while both are -inf
+      if (__any(need)) {
+        const float alpha = need ? fast_exp2((m_run - m_new) * c_l2) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = 32 * db + n;
-      const uint16_t* vp = Vt + d * BN;
-      const int sw = v_swz(d);
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r2 = 0; r2 < 16; ++r2) o[db][r2] *= alpha;
+      }
+      const float mb = m_run == -INFINITY ? 0.0f : m_run * c_l2;
+      u32x4 pb[2][2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        if (!act[sub]) continue;
+        float pv[16];
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) {
+          pv[r2] = fast_exp2(fmaf(s[sub][r2], c_l2, -mb));
+          l_run += pv[r2];
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2)
+            pb[sub][t][q2] = pack2<IS_BF16>(pv[8 * t + 2 * q2], pv[8 * t + 2 * q2 + 1]);
+      }
+
+      // ---- O^T += V^T P^T: consecutive MFMAs update different accumulators ----
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         if (!act[sub]) continue;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int chunk = 4 * sub + 2 * t + h2;
-          const u32x4 vf = *reinterpret_cast<const u32x4*>(vp + 8 * (chunk ^ sw));
-          o[db] = mma32<IS_BF16>(vf, pb[sub][t], o[db]);
+          const int key0 = 32 * sub + 16 * t + 8 * (tg >> 1) + tj;  // + 4 r
+          const uint32_t vrow0 = lds0 + buf * (2 * TILE * 2) + 2 * TILE + 2 * D * key0;
+          const uint32_t vrow1 = vrow0 + 2 * D * 4;
+          if constexpr (DB == 4) {
+            uint32_t pa[8];
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+              const int chunk = 4 * db + 2 * (tg & 1) + (tc >> 1);
+              pa[2 * db] = vrow0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
+              pa[2 * db + 1] = vrow1 + 16 * (chunk ^ vrow_swz<D>(key0 + 4)) + 8 * (tc & 1);
+            }
+            u32x4 vf[4];
+            lds_tr16x8(vf, pa);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] = mma32<IS_BF16>(vf[db], pb[sub][t], o[db]);
+          } else {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int chunk = 4 * db + 2 * (tg & 1) + (tc >> 1);
+              const uint32_t off0 = 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
+              const uint32_t off1 = 16 * (chunk ^ vrow_swz<D>(key0 + 4)) + 8 * (tc & 1);
+              const u32x4 vf = lds_tr16x2(vrow0 + off0, vrow1 + off1);
+              o[db] = mma32<IS_BF16>(vf, pb[sub][t], o[db]);
+            }
+          }
         }
       }
-    }
+    };
+    if (act0 && act1)
+      tile(std::true_type{});
+    else if (act0 || act1)
+      tile(std::false_type{});
 
-    if (it + 1 < nblk) lstore(buf ^ 1);
-    __syncthreads();
+    // this wave's DMA loads of the next tile have landed; after the barrier
+    // every wave's have, and nobody reads this tile's stage any more
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    tile_barrier();
   }
 
   // ---- epilogue: fold the sink, normalize, narrow, store ----
