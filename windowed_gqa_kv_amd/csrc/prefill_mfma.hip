@@ -67,8 +67,15 @@ __device__ __forceinline__ int key_of_m(int m) {
   const int a = m >> 3, hh = (m >> 2) & 1, c = m & 3;
   return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + c;
 }
-// XOR swizzle of the 16-byte chunks of K row r (conflict-free operand reads).
-__device__ __forceinline__ int k_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
+// XOR swizzle of the 16-byte chunks of K row r: the 16 rows one operand read
+// touches per 16 lanes land on 16 different bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  if constexpr (D == 128)
+    return r & 15;
+  else
+    return (r >> 1) & 7;
+}
 // V tile rows (row-major, 16-byte chunks XOR-swizzled by key): the
 // transposing reads of the P*V operand then hit every bank equally.
 template <int D>
@@ -150,6 +157,48 @@ __device__ __forceinline__ void lds_tr16x8(u32x4 (&v)[4], const uint32_t (&p)[8]
   v[1] = __builtin_bit_cast(u32x4, u64x2{r2, r3});
   v[2] = __builtin_bit_cast(u32x4, u64x2{r4, r5});
   v[3] = __builtin_bit_cast(u32x4, u64x2{r6, r7});
+}
+// Split issue / wait of operand reads, so that the reads of the next batch
+// are in flight while the MFMAs of the current one run.  The wait takes the
+// destination registers as read-write operands: everything that uses them is
+// ordered after it.  LDS reads of one wave complete in order, so lgkmcnt(N)
+// leaves exactly the N most recent reads outstanding (no scalar memory
+// operations are issued inside the loop).
+__device__ __forceinline__ void lds_issue_b128x4(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, uint32_t p0,
+                                                 uint32_t p1, uint32_t p2, uint32_t p3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_b128x4(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3) : "n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_issue_tr16x8(uint64_t (&r)[8], const uint32_t (&p)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_tr16x8(uint64_t (&r)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+               : "n"(N)
+               : "memory");
 }
 // Barrier for waves whose only LDS accesses are the inline-assembly ones:
 // wait for this wave's LDS operations, then meet.  (A fenced barrier would
@@ -242,7 +291,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const int pos = 64 * ii + lane;
       const int r = pos / CPR, slot = pos % CPR;
       const int j = min(kb + r, kv_hi);
-      const int ck = slot ^ k_swz(r);
+      const int ck = slot ^ k_swz<D>(r);
       const int cv = slot ^ vrow_swz<D>(r);
       __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)j * a.k_ss + 8 * ck),
                                        (lds_void*)(&lds[buf][0] + 512 * ii), 16, 0, 0);
@@ -282,18 +331,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const uint32_t kbase = lds0 + buf * (2 * TILE * 2);
       const uint32_t kp0 = kbase + 2 * kr0 * D;
       const uint32_t kp1 = kbase + 2 * (32 + kr0) * D;
-      const int sw0 = k_swz(kr0), sw1 = k_swz(32 + kr0);
+      const int sw0 = k_swz<D>(kr0), sw1 = k_swz<D>(32 + kr0);
       if constexpr (FULL) {
         // both sub-tiles, two k-steps per batch of LDS reads
+        u32x4 kf[2][4];
+        auto issue = [&](int ks, u32x4 (&d)[4]) {
+          lds_issue_b128x4(d[0], d[1], d[2], d[3], kp0 + 16 * ((2 * ks + h2) ^ sw0),
+                           kp1 + 16 * ((2 * ks + h2) ^ sw1), kp0 + 16 * ((2 * ks + 2 + h2) ^ sw0),
+                           kp1 + 16 * ((2 * ks + 2 + h2) ^ sw1));
+        };
+        issue(0, kf[0]);
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2) {
-          u32x4 k00, k10, k01, k11;
-          lds_b128x4(k00, k10, k01, k11, kp0 + 16 * ((2 * ks + h2) ^ sw0), kp1 + 16 * ((2 * ks + h2) ^ sw1),
-                     kp0 + 16 * ((2 * ks + 2 + h2) ^ sw0), kp1 + 16 * ((2 * ks + 2 + h2) ^ sw1));
-          s[0] = mma32<IS_BF16>(k00, qf[ks], s[0]);
-          s[1] = mma32<IS_BF16>(k10, qf[ks], s[1]);
-          s[0] = mma32<IS_BF16>(k01, qf[ks + 1], s[0]);
-          s[1] = mma32<IS_BF16>(k11, qf[ks + 1], s[1]);
+          u32x4 (&cur)[4] = kf[(ks >> 1) & 1];
+          if (ks + 2 < KS) {
+            issue(ks + 2, kf[((ks >> 1) + 1) & 1]);
+            lds_wait_b128x4<4>(cur[0], cur[1], cur[2], cur[3]);
+          } else {
+            lds_wait_b128x4<0>(cur[0], cur[1], cur[2], cur[3]);
+          }
+          s[0] = mma32<IS_BF16>(cur[0], qf[ks], s[0]);
+          s[1] = mma32<IS_BF16>(cur[1], qf[ks], s[1]);
+          s[0] = mma32<IS_BF16>(cur[2], qf[ks + 1], s[0]);
+          s[1] = mma32<IS_BF16>(cur[3], qf[ks + 1], s[1]);
         }
       } else {
 #pragma unroll
@@ -366,6 +426,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
 
       // ---- O^T += V^T P^T: consecutive MFMAs update different accumulators ----
+      if constexpr (FULL && DB == 4) {
+        // the four 16-key steps, the reads of the next one in flight during
+        // the MFMAs of the current one
+        uint64_t vr[2][8];
+        auto vaddr = [&](int st, uint32_t (&pa)[8]) {
+          const int sub = st >> 1, t = st & 1;
+          const int key0 = 32 * sub + 16 * t + 8 * (tg >> 1) + tj;
+          const uint32_t vrow0 = lds0 + buf * (2 * TILE * 2) + 2 * TILE + 2 * D * key0;
+          const uint32_t vrow1 = vrow0 + 2 * D * 4;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int chunk = 4 * db + 2 * (tg & 1) + (tc >> 1);
+            pa[2 * db] = vrow0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
+            pa[2 * db + 1] = vrow1 + 16 * (chunk ^ vrow_swz<D>(key0 + 4)) + 8 * (tc & 1);
+          }
+        };
+        {
+          uint32_t pa[8];
+          vaddr(0, pa);
+          lds_issue_tr16x8(vr[0], pa);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          uint64_t (&cur)[8] = vr[st & 1];
+          if (st + 1 < 4) {
+            uint32_t pa[8];
+            vaddr(st + 1, pa);
+            lds_issue_tr16x8(vr[(st + 1) & 1], pa);
+            lds_wait_tr16x8<8>(cur);
+          } else {
+            lds_wait_tr16x8<0>(cur);
+          }
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            o[db] = mma32<IS_BF16>(__builtin_bit_cast(u32x4, u64x2{cur[2 * db], cur[2 * db + 1]}),
+                                   pb[st >> 1][st & 1], o[db]);
+        }
+        return;
+      }
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         if (!act[sub]) continue;
