@@ -3,11 +3,11 @@
 Default workload: single-token decode, bf16, B=8, Hq=32, Hkv=8, D=128, KV
 capacity 4096, seqlens_k ~ integers[1024, 4096), smooth_softmax (zero sink),
 window off.  One step = the whole decode path for one batch: gqa_append_kv
-(the new token's K/V into the cache) then gqa_decode (split-KV attention +
-combine).  Inputs are resident in HBM before timing starts.  Every step
-works on a different replica of the KV cache (R replicas, >= 1 GiB in
-total), so a step cannot be served from the 256 MB Infinity Cache left warm
-by the previous one.
+(the new token's K/V into the cache) then gqa_decode (split-KV attention and
+the merge of the splits, one kernel).  Inputs are resident in HBM before
+timing starts.  Every step works on a different replica of the KV cache (R
+replicas, >= 1 GiB in total), so a step cannot be served from the 256 MB
+Infinity Cache left warm by the previous one.
 
 Prints ONE JSON line.  `value` = algorithmic bytes of the step (K/V rows of
 the kept key range, Q, O, and the appended rows) / wall time per step.
@@ -239,7 +239,7 @@ def main():
                    "curr": w.Lq, "kv_capacity": w.Lk, "window": w.window,
                    "seqlens_k": [int(x) for x in r["inputs"]["seqlens_k"].numpy()],
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gqa_decode (split + combine)",
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel (gqa_decode: split-KV stream with fused combine)",
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": _traffic("decode", w.name, dec_src),
