@@ -1,12 +1,15 @@
 """Summaries of rocprofv3 output for the roofline numbers that bench.py reports.
 
-    python -m windowed_gqa_kv_amd.profiling stats DIR
-        Markdown table of the kernel durations in DIR/*kernel_stats.csv.
+    python -m windowed_gqa_kv_amd.profiling stats DIR [--by-grid]
+        Markdown table of the kernel durations in DIR/*kernel_stats.csv, or,
+        with --by-grid, from DIR/*kernel_trace.csv with one row per (kernel,
+        grid size), which tells apart the workloads that launch one kernel.
 
     python -m windowed_gqa_kv_amd.profiling traffic --fetch DIR --write DIR \\
             --cal-fetch DIR --cal-write DIR --cal-mib N --kernel PATTERN \\
-            --cal-kernel PATTERN --workload NAME --key KEY --out FILE
-        HBM bytes per launch of the kernels whose names contain PATTERN, from
+            --cal-kernel PATTERN --workload NAME --key KEY --out FILE [--grid N]
+        HBM bytes per launch of the kernels whose names contain PATTERN (and,
+        with --grid, whose grid holds N work-items), from
         two counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).  Each
         counter is scaled by what it reads for a plain copy of N MiB (kernels
         matching the calibration pattern) so that a counter which reports a
@@ -57,13 +60,28 @@ def kernel_stats(d: str):
     return rows
 
 
-def counter_mean(d: str, counter: str, pattern: str):
+def kernel_stats_by_grid(d: str):
+    """Rows of *kernel_trace.csv grouped by (name, grid work-items):
+    (name, grid, calls, avg_us, min_us, max_us)."""
+    groups = {}
+    with open(_one(os.path.join(d, "**", "*kernel_trace.csv"))) as f:
+        for r in csv.DictReader(f):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault((r["Kernel_Name"], grid), []).append(us)
+    return [(name, grid, len(v), sum(v) / len(v), min(v), max(v)) for (name, grid), v in groups.items()]
+
+
+def counter_mean(d: str, counter: str, pattern: str, grid: int = 0):
     """Mean per-dispatch value (KiB for *_SIZE counters) and dispatch count of
-    `counter` over the kernels whose names contain `pattern`."""
+    `counter` over the kernels whose names contain `pattern` (and whose grid
+    holds `grid` work-items, if nonzero)."""
     vals = {}
     with open(_one(os.path.join(d, "**", "*counter_collection.csv"))) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter or pattern not in r["Kernel_Name"]:
+                continue
+            if grid and int(r["Grid_Size"]) != grid:
                 continue
             # one row per dispatch (and counter); sum in case a counter is split
             key = r["Dispatch_Id"]
@@ -78,14 +96,22 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    s.add_argument("--by-grid", action="store_true")
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "cal_fetch", "cal_write", "kernel", "cal_kernel", "workload", "key", "out"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
     t.add_argument("--cal-mib", type=float, required=True)
     t.add_argument("--sources", default="decode_mfma.hip,common.h,kernels.h")
     t.add_argument("--command", default="")
+    t.add_argument("--grid", type=int, default=0)
     a = ap.parse_args(argv)
 
+    if a.cmd == "stats" and a.by_grid:
+        print("| kernel | grid work-items | calls | avg us | min us | max us |")
+        print("|---|---|---|---|---|---|")
+        for name, grid, calls, avg, mn, mx in sorted(kernel_stats_by_grid(a.dir), key=lambda r: -r[2] * r[3]):
+            print(f"| `{name}` | {grid} | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} |")
+        return 0
     if a.cmd == "stats":
         print("| kernel | calls | avg us | min us | max us |")
         print("|---|---|---|---|---|")
@@ -93,14 +119,14 @@ def main(argv=None):
             print(f"| `{name}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} |")
         return 0
 
-    fetch_kib, n_f = counter_mean(a.fetch, "FETCH_SIZE", a.kernel)
-    write_kib, n_w = counter_mean(a.write, "WRITE_SIZE", a.kernel)
+    fetch_kib, n_f = counter_mean(a.fetch, "FETCH_SIZE", a.kernel, a.grid)
+    write_kib, n_w = counter_mean(a.write, "WRITE_SIZE", a.kernel, a.grid)
     cal_f, _ = counter_mean(a.cal_fetch, "FETCH_SIZE", a.cal_kernel)
     cal_w, _ = counter_mean(a.cal_write, "WRITE_SIZE", a.cal_kernel)
     true_kib = a.cal_mib * 1024.0
     f_scale, w_scale = true_kib / cal_f, true_kib / cal_w
     rec = {
-        "kernel": a.kernel, "workload": a.workload,
+        "kernel": a.kernel, "workload": a.workload, "grid": a.grid or None,
         "fetch_kib_per_dispatch": round(fetch_kib, 1), "write_kib_per_dispatch": round(write_kib, 1),
         "dispatches": [n_f, n_w],
         "copy_calibration": {"mib": a.cal_mib, "fetch_kib": round(cal_f, 1), "write_kib": round(cal_w, 1),
