@@ -259,6 +259,29 @@ def test_decode_workspace_reuse_across_shapes(gpu):
             compare(out, oracle_decode(w, d), "bf16", f"reuse {rep} {w}")
 
 
+@pytest.mark.parametrize("B,lengths", [
+    (16, "uniform"), (17, "uniform"),
+    (8, [0, 1, 2, 5, 3000, 15, 2999, 1]), (3, [3071, 0, 40]),
+])
+def test_decode_split_modes(gpu, B, lengths):
+    """Both ways the decode kernel cuts its work: with at least two workgroups
+    per (batch, KV head, 16-row) tile every tile gets whole workgroups in
+    proportion to its keys, otherwise the slices are cuts of the flattened key
+    list.  On a 256-workgroup grid, 16 * 8 = 128 tiles take the first and
+    17 * 8 = 136 the second; the listed lengths make tiles of very different
+    sizes (one key up to 3072 keys) under the first."""
+    seed = zlib.crc32(repr(("split", B, lengths)).encode())
+    rng = np.random.default_rng(seed)
+    cap = 3072
+    seq = rng.integers(0, 640, size=B).tolist() if lengths == "uniform" else lengths
+    Hkv = 8 if lengths == "uniform" else 2
+    w = Workload("split", "decode", "bf16", B=B, Hq=4 * Hkv, Hkv=Hkv, D=128, Lq=1, Lk=cap,
+                 window=-1, smooth_softmax=True, seqlens=("list", seq), seed=seed)
+    d = generate(w)
+    out, _, _ = gpu_decode(w, d)
+    compare(out, oracle_decode(w, d), "bf16", f"decode {w}")
+
+
 @pytest.mark.parametrize("B,Hkv,curr", [(32, 16, 16), (33, 16, 16)])
 def test_decode_many_row_tiles(gpu, B, Hkv, curr):
     """Many (batch, KV head, 16-row) tiles in one call: 32*16*4 = 2048 tiles is

@@ -17,14 +17,18 @@
 //
 // Schedule: one balanced round.  A row tile is 16 query rows of one (batch,
 // KV head); its keys are the union of its rows' allowed intervals, cut into
-// 16-key units.  Every workgroup computes the same prefix sum of units over
-// all row tiles (the lengths live on the device) and takes an equal
-// contiguous slice of the flattened unit list; the grid is exactly as many
-// workgroups as the GPU holds at once, so all of them stream from the first
-// microsecond and finish together.  A slice may cross tile boundaries; each
-// piece (slice x tile) leaves one fp32 partial (acc, max, sum).  At the end
-// every workgroup bumps the arrival counter of each tile it touched; the last
-// arrival of a tile merges its partials, folds the sink and writes O.
+// 16-key units.  Every workgroup computes the same split of the units (the
+// lengths live on the device); the grid is exactly as many workgroups as the
+// GPU holds at once, so all of them stream from the first microsecond and
+// finish together.  With at least two workgroups per row tile, each tile
+// gets whole workgroups in proportion to its units and every slice stays
+// inside one tile (a slice that crosses a tile boundary drains its stream
+// there).  With fewer, the slices are equal cuts of the flattened unit list
+// and may cross tile boundaries.  Each piece (slice x tile) leaves one fp32
+// partial (acc, max, sum).  At the end every workgroup bumps the arrival
+// counter of each tile it touched; the last arrival of a tile merges its
+// partials, folds the sink and writes O.  Each merge is the work of one wave,
+// so a workgroup that completes several tiles merges them side by side.
 //
 // Per 16-key unit: each wave streams its units into a private ring of LDS
 // stages with wave-wide LDS DMA loads (global_load_lds_dwordx4: 1 KB per
@@ -50,14 +54,17 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr int kMaxTiles = 2048;       // row tiles per call on this path
 constexpr int kMaxGrid = 2048;        // workgroups per launch (upper bound)
 
-// LDS staging of one wave: kStages units of K and V, 32 KB in flight.
+// LDS staging of one wave: kStages units of K and V in flight, 16 KB per
+// wave for head sizes up to 128 (two workgroups share a CU, so one wave's
+// softmax overlaps another's loads) and 32 KB at head size 256 (two stages of
+// 16 KB units; one workgroup per CU).
 template <int D>
 struct Ring {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kSlots = D / 8;                     // 16-byte chunks per key row
   static constexpr int kUnitBytes = kSub * kRowBytes;      // K (or V) bytes of one unit
   static constexpr int kDmaPerUnit = kUnitBytes / 1024;    // wave-wide 16-byte DMA loads
-  static constexpr int kStages = 32768 / (2 * kUnitBytes);
+  static constexpr int kStages = (D >= 256 ? 32768 : 16384) / (2 * kUnitBytes);
   static constexpr int kWaveBytes = kStages * 2 * kUnitBytes;
   static_assert(kUnitBytes % 1024 == 0, "a unit is whole DMA instructions");
   static_assert((kStages - 1) * 2 * kDmaPerUnit <= 63, "vmcnt range");
@@ -204,6 +211,131 @@ __device__ __forceinline__ void store_row4(const AttnArgs& a, int b, int h, int 
   *reinterpret_cast<u32x2*>(op) = u32x2{pack2<IS_BF16>(x[0], x[1]), pack2<IS_BF16>(x[2], x[3])};
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts within
+// each row of 16 lanes, then the totals of the lower rows (read lanes).
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+__device__ __forceinline__ int wave_sum(int v, int lane) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v, lane), 63);
+}
+// floor(x * i / n) for 0 <= x < 2^31 and 0 <= i, n <= 2048, in 32-bit integers.
+__device__ __forceinline__ int mul_div(int x, int i, int n) {
+  const int q = x / n, r = x - q * n;
+  return q * i + (r * i) / n;
+}
+
+// Merge of one row tile's split partials by one wave (no barriers, no LDS):
+// log-sum-exp over the splits, sink folded into the denominator, normalised,
+// narrowed with round-to-nearest-even and stored.  Split x of the tile is the
+// partial at gpart + x * PART (acc [16][D], then 16 maxima in log2 units,
+// then 16 sums).  Lanes are laid out as (row, split group, chunk of 8 output
+// quads): each lane merges its split group's partials for its chunk, batches
+// of NB splits in flight at once, and the split groups of a row are then
+// combined with shuffles.
+template <bool IS_BF16, int D>
+__device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt, int tt,
+                                           const float* __restrict__ gpart, int nvalid, int lane) {
+  constexpr int PART = kRowsPerTile * D + 2 * kRowsPerTile;
+  constexpr int Q4 = D / 4;        // output quads per row
+  constexpr int QPL = 8;           // quads per lane and pass
+  constexpr int NC = Q4 / QPL;     // chunks per row
+  constexpr int NB = 4;            // splits per lane in flight
+  static_assert(Q4 % QPL == 0, "whole chunks");
+  // the other workgroups' write-through stores were complete before their
+  // arrivals, which this workgroup has seen: acquire once before reading
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // the tile's coordinates (no lengths needed here)
+  const int bg = tt / nrt, rt = tt - bg * nrt;
+  const int xb = bg / a.Hkv, xg = bg - xb * a.Hkv;
+  const int R = min(kRowsPerTile, rows - kRowsPerTile * rt);
+  const int lrp = R <= 1 ? 0 : (R <= 2 ? 1 : (R <= 4 ? 2 : (R <= 8 ? 3 : 4)));  // log2 of padded rows
+  const int L = 64 >> lrp;           // lanes per row
+  const int r = lane >> (6 - lrp);
+  const int sub = lane & (L - 1);
+  const int CL = min(L, NC);         // lanes of a row on distinct chunks
+  const int SG = L / CL;             // split groups per row
+  const int sg = sub / CL;
+  const bool row_ok = r < R;
+  const int rr = row_ok ? r : 0;
+  const int row = kRowsPerTile * rt + rr;
+  const int h = xg * a.G + row % a.G;
+  const float sink = a.use_sink ? sink_log2(a, h) : 0.0f;
+  for (int c = sub % CL; c < NC; c += CL) {
+    float M = -INFINITY, Ls = 0.0f;
+    f32x4 acc[QPL];
+#pragma unroll
+    for (int q = 0; q < QPL; ++q) acc[q] = f32x4{};
+    for (int x0 = sg; x0 < nvalid; x0 += SG * NB) {
+      float mv[NB], lv[NB];
+      f32x4 v[NB][QPL];
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        const int xs = min(x0 + e * SG, nvalid - 1);  // clamped: in bounds, ignored below
+        const float* p = gpart + (int64_t)xs * PART;
+        mv[e] = p[kRowsPerTile * D + rr];
+        lv[e] = p[kRowsPerTile * D + kRowsPerTile + rr];
+#pragma unroll
+        for (int q = 0; q < QPL; ++q) v[e][q] = *reinterpret_cast<const f32x4*>(p + rr * D + 4 * (c * QPL + q));
+      }
+      float mb = M;
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        if (x0 + e * SG >= nvalid) mv[e] = -INFINITY;
+        mb = fmaxf(mb, mv[e]);
+      }
+      if (mb == -INFINITY) continue;  // nothing seen yet by this lane
+      const float fa = fast_exp2(M - mb);  // 0 while M is -inf
+      Ls *= fa;
+#pragma unroll
+      for (int q = 0; q < QPL; ++q) acc[q] *= fa;
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        const float f = fast_exp2(mv[e] - mb);  // 0 for empty or ignored splits
+        Ls += (mv[e] == -INFINITY ? 0.0f : lv[e]) * f;
+#pragma unroll
+        for (int q = 0; q < QPL; ++q) acc[q] += v[e][q] * f;
+      }
+      M = mb;
+    }
+    // combine the split groups of the row (lanes sub ^ CL, sub ^ 2 CL, ...)
+    for (int off = CL; off < L; off <<= 1) {
+      const float Mo = __shfl_xor(M, off, 64);
+      const float Lo = __shfl_xor(Ls, off, 64);
+      const float Mn = fmaxf(M, Mo);
+      const float fa = Mn == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+      const float fb = Mn == -INFINITY ? 0.0f : fast_exp2(Mo - Mn);
+      Ls = Ls * fa + Lo * fb;
+#pragma unroll
+      for (int q = 0; q < QPL; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[q][e] = acc[q][e] * fa + __shfl_xor(acc[q][e], off, 64) * fb;
+      M = Mn;
+    }
+    if (row_ok && sg == 0) {
+      float fac;
+      if (M == -INFINITY) {
+        fac = 0.0f;
+      } else if (a.use_sink) {
+        const float M2 = fmaxf(M, sink);
+        const float e1 = fast_exp2(M - M2);
+        fac = e1 / (Ls * e1 + fast_exp2(sink - M2));
+      } else {
+        fac = 1.0f / Ls;
+      }
+#pragma unroll
+      for (int q = 0; q < QPL; ++q) store_row4<IS_BF16, D>(a, xb, h, row / a.G, 4 * (c * QPL + q), acc[q] * fac);
+    }
+  }
+}
+
 template <bool IS_BF16, int D, bool SOFTCAP>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int nrt,
                                                      float* __restrict__ part, unsigned* __restrict__ counters) {
@@ -213,14 +345,12 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   constexpr int S = RG::kStages;
   constexpr int PART = kRowsPerTile * D + 2 * kRowsPerTile;  // floats per partial
   constexpr int MERGE = D / 4 + 2;                            // floats per lane in a merge slot
-  constexpr int XB = 64;                                      // partials per combine batch
-  // The rings hold the LDS stages while streaming, the wave merge slots
-  // between pieces and the combine's per-split maxima and sums at the end.
+  // The rings hold the LDS stages while streaming and the wave merge slots
+  // between pieces.
   static_assert(2 * MERGE * 64 * 4 <= kWaves * RG::kWaveBytes, "merge slots fit the rings");
-  static_assert((2 * XB * kRowsPerTile + 4 * kRowsPerTile) * 4 <= kWaves * RG::kWaveBytes, "combine fits");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kWaves * RG::kWaveBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds[kRowsPerTile * 2 * D];  // Q tile, swizzled like K
-  __shared__ int pre[kMaxTiles + 1];  // unit prefix sum over tiles
+  __shared__ int pre[kMaxTiles + 2];  // unit prefix sum over tiles (then workgroups per tile)
   __shared__ int wsum[4];
   __shared__ int flag[256];
   float (*merge_lds)[MERGE * 64] = reinterpret_cast<float (*)[MERGE * 64]>(&ring[0]);
@@ -234,29 +364,24 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   const int k = blockIdx.x;
   const int T = a.B * a.Hkv * nrt;
 
-  // ---- prefix sum of 16-key units over all row tiles (same in every workgroup) ----
-  {
+  // ---- the split of the work (the same in every workgroup) ----
+  // Exclusive prefix sum of f(t) over the row tiles into out[0..T].
+  auto block_scan = [&](int* out, auto f) {
     int carry = 0;
-    if (tid == 0) pre[0] = 0;
+    if (tid == 0) out[0] = 0;
     for (int base = 0; base < T; base += 256) {
       const int t = base + tid;
-      int u = 0;
-      if (t < T) u = units_of(make_tile(a, rows, nrt, t));
-      int incl = u;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
+      const int incl = wave_incl_scan(t < T ? f(t) : 0, lane);
       if (lane == 63) wsum[w] = incl;
       __syncthreads();
       int before = carry;
       for (int x = 0; x < w; ++x) before += wsum[x];
-      if (t < T) pre[t + 1] = before + incl;
+      if (t < T) out[t + 1] = before + incl;
       carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
       __syncthreads();
     }
-  }
+  };
+  block_scan(pre, [&](int t) { return units_of(make_tile(a, rows, nrt, t)); });
   const int U = pre[T];
 
   // tiles nobody streams (no allowed key for any of their rows) output zeros
@@ -268,17 +393,62 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       store_row4<IS_BF16, D>(a, x.b, x.g * a.G + row % a.G, row / a.G, 4 * (idx % (D / 4)), f32x4{});
     }
   }
-  // Slices: workgroup k < Gs streams units [floor(U k / Gs), floor(U (k+1) / Gs)).
-  // With Gs <= U no slice is empty, so the owners of a tile's units are
-  // exactly the consecutive workgroups between its first and last owner.
-  const int Gs = min(G, U);
-  if (k >= Gs) return;
 
-  const int ustart = (int)((int64_t)U * k / Gs);
-  const int uend = (int)((int64_t)U * (k + 1) / Gs);
-  // first tile holding unit ustart: the largest t with pre[t] <= ustart
-  int t_first = 0;
-  {
+  // Slices.  With at least two workgroups per row tile, tile t gets
+  // n_t = ceil(u_t / L) workgroups of its own (u_t its units, L the smallest
+  // load for which they fit the grid) and its units are cut evenly among them:
+  // no slice crosses a tile boundary, where a workgroup's stream would drain
+  // and restart.  Otherwise workgroup k < Gs streams units
+  // [floor(U k / Gs), floor(U (k+1) / Gs)) of the tiles' concatenation.
+  // Either way no slice is empty and the workgroups holding a tile's units
+  // are consecutive.
+  const bool aligned = 2 * T <= G;
+  int* const pren = pre + T + 1;  // aligned: prefix sum of n_t (2T + 2 <= kMaxTiles + 2 entries)
+  int Gs;
+  if (aligned) {
+    // L = ceil(U / (G - T)) always fits, since sum_t ceil(u_t / L) < U / L + T
+    int lo = max(1, (U + G - 1) / G), hi = max(1, (U + (G - T) - 1) / (G - T));
+    // every wave runs the search on its own (same result, no barriers)
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      int c = 0;
+      for (int t = lane; t < T; t += 64) c += (pre[t + 1] - pre[t] + mid - 1) / mid;
+      if (wave_sum(c, lane) <= G) hi = mid; else lo = mid + 1;
+    }
+    const int L = lo;
+    block_scan(pren, [&](int t) { return (pre[t + 1] - pre[t] + L - 1) / L; });
+    Gs = pren[T];
+  } else {
+    Gs = min(G, U);
+  }
+  if (k >= Gs) return;
+  // workgroups first .. first + nvalid - 1 hold the units of (non-empty) tile t
+  auto contributors = [&](int t, int& first, int& nvalid) {
+    if (aligned) {
+      first = pren[t];
+      nvalid = pren[t + 1] - pren[t];
+    } else {
+      first = owner_of(pre[t], U, Gs);
+      nvalid = owner_of(pre[t + 1] - 1, U, Gs) - first + 1;
+    }
+  };
+
+  int ustart, uend, t_first;
+  if (aligned) {
+    int lo = 0, hi = T;  // invariant: pren[lo] <= k < pren[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pren[mid] <= k) lo = mid; else hi = mid;
+    }
+    t_first = lo;
+    const int ut = pre[lo + 1] - pre[lo];
+    const int n = pren[lo + 1] - pren[lo], i = k - pren[lo];
+    ustart = pre[lo] + mul_div(ut, i, n);
+    uend = pre[lo] + mul_div(ut, i + 1, n);
+  } else {
+    ustart = mul_div(U, k, Gs);
+    uend = mul_div(U, k + 1, Gs);
+    // first tile holding unit ustart: the largest t with pre[t] <= ustart
     int lo = 0, hi = T;  // invariant: pre[lo] <= ustart < pre[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -502,166 +672,40 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  float* lf = reinterpret_cast<float*>(&ring[0]);  // [XB][16] maxima, then factors
-  float* ls = lf + XB * kRowsPerTile;                     // [XB][16] sums
-  float* rowM = ls + XB * kRowsPerTile;
-  float* rowL = rowM + kRowsPerTile;
-  float* rowA = rowL + kRowsPerTile;
-  float* rowS = rowA + kRowsPerTile;
-  bool acquired = false;
   for (int base = t_first; base <= t_last; base += 256) {
-  // one arrival per touched tile, all in flight together
-  const int nbt = min(256, t_last - base + 1);
-  if (tid < nbt) {
-    const int tt = base + tid;
-    int f = 0;
-    if (pre[tt + 1] != pre[tt]) {
-      const int nvalid = owner_of(pre[tt + 1] - 1, U, Gs) - owner_of(pre[tt], U, Gs) + 1;
-      f = __hip_atomic_fetch_add(&counters[tt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-          (unsigned)(nvalid - 1);
-    }
-    flag[tid] = f;
-  }
-  __syncthreads();
-  for (int i = 0; i < nbt; ++i) {
-    if (!flag[i]) continue;
-    const int tt = base + i;
-    const int first = owner_of(pre[tt], U, Gs);
-    const int nvalid = owner_of(pre[tt + 1] - 1, U, Gs) - first + 1;
-    if (!acquired) {
-      // acquire at device scope once: the plain loads below then see the
-      // other workgroups' write-through stores
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      acquired = true;
-    }
-    const Tile x = make_tile(a, rows, nrt, tt);
-    const float* gpart = part + (int64_t)(first + tt) * PART;
-
-    // Merge the nvalid partials in batches.  Per batch: (1) every thread
-    // issues the loads of all its partial accumulators of the batch (output
-    // quads x splits, clamped indices, all in flight together), then (2) the
-    // per-(split, row) maxima and sums are fetched into LDS -- one round trip
-    // for both; (3) one thread per row moves the row's running max, rescales
-    // its running sum and turns the batch's maxima into factors exp2(m_x - M);
-    // (4) TQ threads per output quad accumulate factor * acc over disjoint
-    // splits (all relative to the same M), reduced with shuffles at the end.
-    const int items = x.rows_tile * (D / 4);
-    // threads per output quad: the largest power of two with items * TQ <= 256
-    const int TQ = items <= 16 ? 16 : (items <= 32 ? 8 : (items <= 64 ? 4 : (items <= 128 ? 2 : 1)));
-    const int t_sub = tid % TQ;
-    constexpr int IPT = (kRowsPerTile * (D / 4) + 255) / 256;  // output quads per thread when TQ == 1
-    constexpr int NPT = 32 / IPT;                               // splits per output quad and batch
-    const int XBt = min(XB, NPT * TQ);
-    int it_r[IPT], it_d[IPT];
-    bool it_ok[IPT];
-#pragma unroll
-    for (int q = 0; q < IPT; ++q) {
-      const int item = (tid / TQ) + q * (256 / TQ);
-      it_ok[q] = item < items;
-      const int ic = it_ok[q] ? item : 0;
-      it_r[q] = ic / (D / 4);
-      it_d[q] = ic % (D / 4);
-    }
-    // sink logits of the tile's rows, fetched now so that the load overlaps the partials'
-    float sink_row = 0.0f;
-    if (a.use_sink && tid < x.rows_tile) {
-      const int row = kRowsPerTile * x.rt + tid;
-      sink_row = sink_log2(a, x.g * a.G + row % a.G);
-    }
-    f32x4 acc[IPT];
-#pragma unroll
-    for (int q = 0; q < IPT; ++q) acc[q] = f32x4{};
-    if (tid < kRowsPerTile) {
-      rowM[tid] = -INFINITY;
-      rowL[tid] = 0.0f;
-    }
-    for (int xb = 0; xb < nvalid; xb += XBt) {
-      const int nb = min(XBt, nvalid - xb);
-      f32x4 v[IPT][NPT];
-#pragma unroll
-      for (int q = 0; q < IPT; ++q)
-#pragma unroll
-        for (int e = 0; e < NPT; ++e) {
-          const int xs = min(t_sub + e * TQ, nb - 1);
-          v[q][e] = *reinterpret_cast<const f32x4*>(gpart + (int64_t)(xb + xs) * PART + it_r[q] * D + 4 * it_d[q]);
-        }
-      // the previous batch's factor reads are complete before they are
-      // overwritten (LDS-only fences: no DMA load is in flight here)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-      for (int pr = tid; pr < nb * x.rows_tile; pr += 256) {
-        const int xs = pr / x.rows_tile, r = pr % x.rows_tile;
-        const float* p = gpart + (int64_t)(xb + xs) * PART + kRowsPerTile * D;
-        lf[xs * kRowsPerTile + r] = p[r];
-        ls[xs * kRowsPerTile + r] = p[kRowsPerTile + r];
+    // one arrival per touched tile, all in flight together
+    const int nbt = min(256, t_last - base + 1);
+    if (tid < nbt) {
+      const int tt = base + tid;
+      int f = 0;
+      if (pre[tt + 1] != pre[tt]) {
+        int first, nvalid;
+        contributors(tt, first, nvalid);
+        f = __hip_atomic_fetch_add(&counters[tt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (unsigned)(nvalid - 1);
       }
-      __syncthreads();
-      if (tid < x.rows_tile) {
-        const int r = tid;
-        float mb = -INFINITY;
-        for (int xs = 0; xs < nb; ++xs) mb = fmaxf(mb, lf[xs * kRowsPerTile + r]);
-        const float Mo = rowM[r];
-        const float Mn = fmaxf(Mo, mb);
-        float L = 0.0f, alpha = 1.0f;
-        if (Mn != -INFINITY) {
-          alpha = fast_exp2(Mo - Mn);  // 0 while nothing was seen
-          L = rowL[r] * alpha;
-          for (int xs = 0; xs < nb; ++xs) {
-            const float f = fast_exp2(lf[xs * kRowsPerTile + r] - Mn);
-            lf[xs * kRowsPerTile + r] = f;
-            L += ls[xs * kRowsPerTile + r] * f;
-          }
-        } else {
-          for (int xs = 0; xs < nb; ++xs) lf[xs * kRowsPerTile + r] = 0.0f;
-        }
-        rowM[r] = Mn;
-        rowL[r] = L;
-        rowA[r] = alpha;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < IPT; ++q) {
-        if (!it_ok[q]) continue;
-        const int r = it_r[q];
-        acc[q] *= rowA[r];
-#pragma unroll
-        for (int e = 0; e < NPT; ++e) {
-          const int xs = t_sub + e * TQ;
-          acc[q] += v[q][e] * (xs < nb ? lf[xs * kRowsPerTile + r] : 0.0f);
-        }
-      }
+      flag[tid] = f;
     }
-    if (tid < x.rows_tile) rowS[tid] = sink_row;
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < IPT; ++q) {
-      for (int off = TQ / 2; off > 0; off >>= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[q][e] += __shfl_xor(acc[q][e], off, 64);
-      if (!it_ok[q] || t_sub != 0) continue;
-      const int r = it_r[q], dq = it_d[q];
-      const int row = kRowsPerTile * x.rt + r;
-      const int h = x.g * a.G + row % a.G;
-      const float M = rowM[r], L = rowL[r];
-      float fac;
-      if (M == -INFINITY) {
-        fac = 0.0f;
-      } else if (a.use_sink) {
-        const float tsk = rowS[r];
-        const float M2 = fmaxf(M, tsk);
-        const float e1 = fast_exp2(M - M2);
-        fac = e1 / (L * e1 + fast_exp2(tsk - M2));
-      } else {
-        fac = 1.0f / L;
+    // The tiles this workgroup completed go to its waves in turn, so that
+    // their merges run side by side.
+    int cnt = 0;
+    for (int c0 = 0; c0 < nbt; c0 += 64) {
+      uint64_t mask = __ballot(c0 + lane < nbt && flag[c0 + lane]);
+      while (mask) {
+        const int i = c0 + __builtin_ctzll(mask);
+        mask &= mask - 1;
+        if (cnt++ % kWaves != w) continue;
+        const int tt = base + i;
+        int first, nvalid;
+        contributors(tt, first, nvalid);
+        nvalid = min(nvalid, Gs - first);  // never past the slots this call wrote
+        merge_tile<IS_BF16, D>(a, rows, nrt, tt, part + (int64_t)(first + tt) * PART, nvalid, lane);
+        if (lane == 0)  // ready for the next call
+          __hip_atomic_store(&counters[tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      store_row4<IS_BF16, D>(a, x.b, h, row / a.G, 4 * dq, acc[q] * fac);
     }
-    if (tid == 0)  // ready for the next call
-      __hip_atomic_store(&counters[tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-  }
-  __syncthreads();  // flag[] is rewritten by the next batch of tiles
+    __syncthreads();  // flag[] is rewritten by the next batch of tiles
   }
 }
 
