@@ -124,22 +124,17 @@ __device__ __forceinline__ float half_to_f32(uint16_t h) {
   if constexpr (IS_BF16) return bf16_to_f32(h); else return f16_to_f32(h);
 }
 
-// Round-to-nearest-even narrowing (v_cvt_pk_bf16_f32 / v_cvt_f16_f32).
+// Round-to-nearest-even narrowing of a pair (one v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <bool IS_BF16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  if constexpr (IS_BF16) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    uint16_t ua, ub;
-    __builtin_memcpy(&ua, &a, 2);
-    __builtin_memcpy(&ub, &b, 2);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
-  } else {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    uint16_t ua, ub;
-    __builtin_memcpy(&ua, &a, 2);
-    __builtin_memcpy(&ub, &b, 2);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
-  }
+  if constexpr (IS_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
 }
 
 // ---------------------------------------------------------------------------
@@ -157,6 +152,12 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Value of lane l ^ 32 (the other half-wave).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// The value of lane i ^ 32, without an LDS round trip: v_permlane32_swap of x
+// with itself leaves the low half's values in both halves of one result and
+// the high half's in both halves of the other.
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 }  // namespace gqa

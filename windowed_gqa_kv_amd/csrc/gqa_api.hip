@@ -192,7 +192,9 @@ GQA_API gqa_status gqa_prefill(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t L
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int dtype = (int)plan->attrs.dtype;
   hipError_t e;
-  if (Lk > 0 && gqa::prefill_mfma_supported(dtype, plan->attrs.head_size))
+  // the matrix-core kernel addresses a 64-row K/V tile with 32-bit offsets
+  const bool small_strides = a.k_ss < (int64_t(1) << 24) && a.v_ss < (int64_t(1) << 24);
+  if (Lk > 0 && small_strides && gqa::prefill_mfma_supported(dtype, plan->attrs.head_size))
     e = gqa::launch_prefill_mfma(a, dtype, plan->attrs.softcap > 0, stream);
   else
     e = gqa::launch_attn_generic(a, dtype, stream);

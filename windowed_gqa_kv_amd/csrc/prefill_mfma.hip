@@ -11,11 +11,13 @@
 // final denominator (same page, section "smooth_softmax / head_sink").
 //
 // Layout of the work.
-//   * Workgroup = 4 waves = 128 query rows of one (batch, query head); wave w
-//     owns rows [32w, 32w+32).  Key tiles of 64 rows of K and of V are copied
+//   * Workgroup = 4 waves.  It holds hw query heads of one KV head (hw = the
+//     largest power of two dividing G, at most 4) and 4 / hw groups of 32
+//     rows of each; wave w owns 32 rows of one head.  All of them read the
+//     same keys, so K and V tiles of 64 rows are loaded once per workgroup:
 //     from global memory straight into LDS by LDS DMA (global_load_lds_dwordx4,
 //     no registers held by loads in flight), double buffered, one barrier per
-//     tile; the 4 waves share them.  Two workgroups fit on a CU.
+//     tile.  Two workgroups fit on a CU.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q held in
 //     registers for the whole kernel), so each lane ends up owning one query
 //     row and 16 keys of every 32-key sub-tile.  The K rows fed to the MFMA M
@@ -25,20 +27,25 @@
 //     an LDS round trip.
 //   * O^T += V^T P^T on the same MFMA: the A operand (8 consecutive keys of one
 //     head-dim column per lane) comes out of the row-major V tile through two
-//     transposing LDS reads (ds_read_b64_tr_b16).  K and V rows are stored with
-//     XOR-swizzled 16-byte chunks (chosen per lane in the DMA source address),
-//     which keeps both read patterns free of bank conflicts.
+//     transposing LDS reads (ds_read_b64_tr_b16), addressed by per-lane
+//     offsets fixed for the whole kernel plus immediates.  K and V rows are
+//     stored with XOR-swizzled 16-byte chunks (chosen per lane in the DMA
+//     source address), which keeps both read patterns free of bank conflicts.
 //   * Operand reads are batched (four K operands, or the four V operands of one
-//     16-key step, per wait) and consecutive MFMAs update different
-//     accumulators; tiles fully inside every row's band take a branch-free
-//     path.
+//     16-key step, per wait) and issued one batch ahead of the MFMAs that use
+//     them; the next tile's DMA loads are spread over the K batches.  Every
+//     tile a wave can see takes one branch-free path; sub-tiles outside all of
+//     its rows' bands are masked like any other excluded key.
 //   * Online softmax in fp32 with exp2, the scale folded into one FMA, a lazy
-//     rescale (the running max only moves when it grows by more than 2^8),
-//     and masks evaluated only on boundary sub-tiles; sub-tiles a wave cannot
-//     see are skipped.
-//   * Work items are ordered (batch, KV head)-major so that the query heads
-//     sharing one K/V land on the same XCD (its own L2), heaviest row blocks
+//     rescale (the running max only moves when it grows by more than 2^8, on
+//     a real branch), masks evaluated only on boundary sub-tiles, and pairs
+//     narrowed by one conversion each.  The vector work per tile is the floor
+//     of the method: the two contractions and their softmax take about the
+//     same issue time per wave.
+//   * Work items are ordered (batch, KV head)-major so that the workgroups of
+//     one KV head land on the same XCD (its own L2), heaviest row blocks
 //     first within each KV head.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -46,7 +53,8 @@
 namespace gqa {
 namespace {
 
-constexpr int BM = 128;  // query rows per workgroup
+constexpr int kWaves = 4;   // waves per workgroup (two workgroups per CU)
+constexpr int NSTAGE = 2;   // K/V tiles in LDS: the current one and the next
 constexpr int BN = 64;   // keys per LDS tile
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
@@ -92,78 +100,15 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 // LDS reads of DMA-filled tiles are inline assembly: the compiler would put a
 // wait for every LDS DMA load in flight (the next tile's) in front of each
-// of them.  Results are consumed whole, as MFMA operands (single elements of
-// a vector-typed inline-asm result are mis-assigned to sub-registers by this
-// compiler); the 64-bit halves of a V operand come back as scalars.
-__device__ __forceinline__ u32x4 lds_b128(uint32_t p) {
-  u32x4 v;
-  asm volatile(
-      "ds_read_b128 %0, %1\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=v"(v)
-      : "v"(p)
-      : "memory");
-  return v;
-}
-__device__ __forceinline__ u32x4 lds_tr16x2(uint32_t p0, uint32_t p1) {
-  uint64_t a, b;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %2\n\t"
-      "ds_read_b64_tr_b16 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a), "=&v"(b)
-      : "v"(p0), "v"(p1)
-      : "memory");
-  return __builtin_bit_cast(u32x4, u64x2{a, b});
-}
-__device__ __forceinline__ void lds_b128x4(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, uint32_t p0,
-                                           uint32_t p1, uint32_t p2, uint32_t p3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
-      : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
-      : "memory");
-}
-__device__ __forceinline__ void lds_b128x2(u32x4& a0, u32x4& a1, uint32_t p0, uint32_t p1) {
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a0), "=&v"(a1)
-      : "v"(p0), "v"(p1)
-      : "memory");
-}
-// Four P*V operands (8 transposing reads), one wait.
-__device__ __forceinline__ void lds_tr16x8(u32x4 (&v)[4], const uint32_t (&p)[8]) {
-  uint64_t r0, r1, r2, r3, r4, r5, r6, r7;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
-      : "memory");
-  v[0] = __builtin_bit_cast(u32x4, u64x2{r0, r1});
-  v[1] = __builtin_bit_cast(u32x4, u64x2{r2, r3});
-  v[2] = __builtin_bit_cast(u32x4, u64x2{r4, r5});
-  v[3] = __builtin_bit_cast(u32x4, u64x2{r6, r7});
-}
-// Split issue / wait of operand reads, so that the reads of the next batch
-// are in flight while the MFMAs of the current one run.  The wait takes the
-// destination registers as read-write operands: everything that uses them is
-// ordered after it.  LDS reads of one wave complete in order, so lgkmcnt(N)
-// leaves exactly the N most recent reads outstanding (no scalar memory
-// operations are issued inside the loop).
+// of them.  Reads are issued and waited for separately, so that the reads of
+// the next batch are in flight while the MFMAs of the current one run; the
+// wait takes the destination registers as read-write operands, so that
+// everything using them is ordered after it.  LDS reads of one wave complete
+// in order, so lgkmcnt(N) leaves exactly the N most recent reads outstanding
+// (no scalar memory operations are issued inside the loop).  Results are
+// consumed whole, as MFMA operands (single elements of a vector-typed
+// inline-asm result are mis-assigned to sub-registers by this compiler); the
+// 64-bit halves of a V operand come back as scalars.
 __device__ __forceinline__ void lds_issue_b128x4(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, uint32_t p0,
                                                  uint32_t p1, uint32_t p2, uint32_t p3) {
   asm volatile(
@@ -179,26 +124,45 @@ template <int N>
 __device__ __forceinline__ void lds_wait_b128x4(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3) : "n"(N) : "memory");
 }
-__device__ __forceinline__ void lds_issue_tr16x8(uint64_t (&r)[8], const uint32_t (&p)[8]) {
+// Transposing reads of the V operands of one 16-key step: for each 32-wide
+// output block db, rows key0 and key0 + 4 (immediate offsets O0 and O1 from
+// the block's per-lane address).
+template <int O0, int O1>
+__device__ __forceinline__ void lds_issue_tr16x8(uint64_t (&r)[8], const uint32_t (&p)[4]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15"
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "n"(O0), "n"(O1)
+      : "memory");
+}
+template <int O0, int O1>
+__device__ __forceinline__ void lds_issue_tr16x4(uint64_t (&r)[4], const uint32_t (&p)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(p[0]), "v"(p[1]), "n"(O0), "n"(O1)
       : "memory");
 }
 template <int N>
-__device__ __forceinline__ void lds_wait_tr16x8(uint64_t (&r)[8]) {
+__device__ __forceinline__ void lds_wait_tr16(uint64_t (&r)[8]) {
   asm volatile("s_waitcnt lgkmcnt(%8)"
                : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
                : "n"(N)
                : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_tr16(uint64_t (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N) : "memory");
 }
 // Barrier for waves whose only LDS accesses are the inline-assembly ones:
 // wait for this wave's LDS operations, then meet.  (A fenced barrier would
@@ -207,43 +171,53 @@ __device__ __forceinline__ void tile_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
 }
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Two waves per SIMD (two workgroups per CU): the register budget is 256.
 template <bool IS_BF16, int D, bool SOFTCAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
-    AttnArgs a, int nrb, int items, int per_xcd) {
+    AttnArgs a, int nrb, int items, int per_xcd, int hw) {
   constexpr int KS = D / 16;    // k-steps of the QK^T contraction
   constexpr int DB = D / 32;    // 32-wide output blocks
   constexpr int CPR = D / 8;    // 16-byte chunks per K row
   constexpr int TILE = BN * D;  // elements of one K (or V) tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NSTAGE][2 * TILE];
 
   // ---- work item: XCD-major, KV-head-major, heavy row blocks first ----
+  // A workgroup holds hw query heads of one KV head (hw divides G, at most 8)
+  // and 8 / hw groups of 32 rows of each: all its waves share every K/V tile.
   const int id = blockIdx.x;
   const int item = (id & 7) * per_xcd + (id >> 3);
   if (item >= items) return;
-  const int per_bg = a.G * nrb;
+  const int ngrp = a.G / hw;  // head groups per KV head
+  const int per_bg = ngrp * nrb;
   const int bg = item / per_bg;
   const int rem = item - bg * per_bg;
-  const int rb = nrb - 1 - rem / a.G;
-  const int hl = rem % a.G;
+  const int rb = nrb - 1 - rem / ngrp;
+  const int hg = rem % ngrp;
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
-  const int h = g * a.G + hl;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int n = lane & 31;
   const int h2 = lane >> 5;
+  const int h = g * a.G + hg * hw + w % hw;  // this wave's query head
+  const int rpw = 32 * (kWaves / hw);        // rows of each head in this workgroup
 
   const BatchSpan sp = batch_span(a, b);
-  const int row0 = rb * BM;
-  const int rows_here = min(BM, a.Lq - row0);
+  const int row0 = rb * rpw;
+  const int rows_here = min(rpw, a.Lq - row0);
   const int kv_lo = row_lo(a, sp.q_off + row0);
   const int kv_hi = row_hi(a, sp.q_off + row0 + rows_here - 1, sp.valid);
 
-  const int wrow0 = row0 + 32 * w;
+  const int wrow0 = row0 + 32 * (w / hw);
   const int wrows = min(32, a.Lq - wrow0);  // may be <= 0
   const int pw0 = sp.q_off + wrow0;
   const int pw1 = pw0 + max(wrows, 1) - 1;
@@ -281,231 +255,244 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // K and V tiles go from global memory straight into LDS (LDS DMA, 1 KB per
   // wave-wide instruction).  Both are row-major with XOR-swizzled 16-byte
   // chunks; lane L of instruction i writes position 64 i + L, so it loads the
-  // global chunk that the swizzle puts there.  Rows past kv_hi are clamped to
+  // global chunk that the swizzle puts there.  The per-lane source offsets
+  // within a tile are the same for every tile; only the tile's base address
+  // (wave-uniform) moves.  In the last tile, rows past kv_hi are clamped to
   // kv_hi: real, finite keys that the masks remove for every row.
-  constexpr int NDMA = TILE * 2 / 1024 / 4;  // per wave, per tile, per tensor
-  auto dma_tile = [&](int kb, int buf) {
+  constexpr int NDMA = TILE * 2 / 1024 / kWaves;  // per wave, per tile, per tensor
+  constexpr int RPI = 64 / CPR;              // tile rows per DMA instruction
+  const int64_t krow_b = a.k_ss * 2, vrow_b = a.v_ss * 2;
+  uint32_t koff[NDMA], voff[NDMA];
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int ii = NDMA * w + i;  // instruction index within the tile
-      const int pos = 64 * ii + lane;
-      const int r = pos / CPR, slot = pos % CPR;
+  for (int i = 0; i < NDMA; ++i) {
+    const int r = RPI * (NDMA * w + i) + lane / CPR, slot = lane % CPR;
+    koff[i] = (uint32_t)(r * krow_b) + 16 * (slot ^ k_swz<D>(r));
+    voff[i] = (uint32_t)(r * vrow_b) + 16 * (slot ^ vrow_swz<D>(r));
+  }
+  // instruction pair i (one K and one V load) of this wave's share of a tile
+  auto dma_part = [&](int kb, int buf, int i) {
+    uint16_t* kdst = &lds[buf][0] + 512 * (NDMA * w + i);
+    uint16_t* vdst = &lds[buf][TILE] + 512 * (NDMA * w + i);
+    if (kb + BN - 1 <= kv_hi) {
+      const char* kbase = reinterpret_cast<const char*>(Kg) + kb * krow_b;
+      const char* vbase = reinterpret_cast<const char*>(Vg) + kb * vrow_b;
+      __builtin_amdgcn_global_load_lds((global_void*)(kbase + koff[i]), (lds_void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(vbase + voff[i]), (lds_void*)vdst, 16, 0, 0);
+    } else {
+      const int r = RPI * (NDMA * w + i) + lane / CPR, slot = lane % CPR;
       const int j = min(kb + r, kv_hi);
-      const int ck = slot ^ k_swz<D>(r);
-      const int cv = slot ^ vrow_swz<D>(r);
-      __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)j * a.k_ss + 8 * ck),
-                                       (lds_void*)(&lds[buf][0] + 512 * ii), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)j * a.v_ss + 8 * cv),
-                                       (lds_void*)(&lds[buf][TILE] + 512 * ii), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)j * a.k_ss + 8 * (slot ^ k_swz<D>(r))),
+                                       (lds_void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)j * a.v_ss + 8 * (slot ^ vrow_swz<D>(r))),
+                                       (lds_void*)vdst, 16, 0, 0);
     }
   };
+  auto dma_tile = [&](int kb, int buf) {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) dma_part(kb, buf, i);
+  };
+  static_assert(NDMA >= 1 && NDMA <= KS / 2, "at most one DMA pair per batch of QK operand reads");
 
   const float c_l2 = SOFTCAP ? 1.0f : a.scale_log2;  // raw units -> log2 units
   const int kr0 = key_of_m(n);                        // this lane's K row in a sub-tile
 
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0];
+  constexpr uint32_t kStage = 2 * TILE * 2;  // bytes of one K + V stage
+  // Per-lane byte offsets (within a stage) of the transposing V reads of
+  // 16-key step 0: rows 8 (g >> 1) + j (+ 4) of the step, columns
+  // 16 (g & 1) + 4 c .. + 3 of each 32-column block.  Step st adds 32 D st
+  // bytes and the second row 8 D; the swizzle is the same for all of them.
+  uint32_t vrd[DB];
+  {
+    const int tg = lane >> 4, tj = (lane >> 2) & 3, tc = lane & 3;
+    const int key0 = 8 * (tg >> 1) + tj;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int chunk = 4 * db + 2 * (tg & 1) + (tc >> 1);
+      vrd[db] = 2 * TILE + 2 * D * key0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
+    }
+  }
+
+  // Sub-tiles (32 keys) of the tile at kb that this wave can see; a tile with
+  // at least one is computed whole, and a sub-tile outside every row's band
+  // is masked out like any other excluded key.
+  auto active = [&](int kb, bool& a0, bool& a1) {
+    a0 = wrows > 0 && kb <= w_hi && kb + 31 >= w_lo;
+    a1 = wrows > 0 && kb + 32 <= w_hi && kb + 63 >= w_lo;
+  };
+
+  // ---- S^T = K Q^T for both sub-tiles, two k-steps per batch of reads; the
+  // DMA pairs of a later tile ride along, one per batch ----
+  auto qk = [&](uint32_t sbase, f32x16 (&sc)[2], auto&& dma_at) {
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
+    const uint32_t kp0 = sbase + 2 * kr0 * D;
+    const uint32_t kp1 = sbase + 2 * (32 + kr0) * D;
+    const int sw0 = k_swz<D>(kr0), sw1 = k_swz<D>(32 + kr0);
+    u32x4 kf[2][4];
+    auto issue = [&](int ks, u32x4 (&d)[4]) {
+      lds_issue_b128x4(d[0], d[1], d[2], d[3], kp0 + 16 * ((2 * ks + h2) ^ sw0),
+                       kp1 + 16 * ((2 * ks + h2) ^ sw1), kp0 + 16 * ((2 * ks + 2 + h2) ^ sw0),
+                       kp1 + 16 * ((2 * ks + 2 + h2) ^ sw1));
+    };
+    issue(0, kf[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) {
+      u32x4 (&cur)[4] = kf[(ks >> 1) & 1];
+      if (ks + 2 < KS) {
+        issue(ks + 2, kf[((ks >> 1) + 1) & 1]);
+        lds_wait_b128x4<4>(cur[0], cur[1], cur[2], cur[3]);
+      } else {
+        lds_wait_b128x4<0>(cur[0], cur[1], cur[2], cur[3]);
+      }
+      if ((ks >> 1) < NDMA) dma_at(ks >> 1);
+      sc[0] = mma32<IS_BF16>(cur[0], qf[ks], sc[0]);
+      sc[1] = mma32<IS_BF16>(cur[1], qf[ks], sc[1]);
+      sc[0] = mma32<IS_BF16>(cur[2], qf[ks + 1], sc[0]);
+      sc[1] = mma32<IS_BF16>(cur[3], qf[ks + 1], sc[1]);
+    }
+  };
+
+  // ---- softmax of one tile's scores, in pieces that can sit between the
+  // MFMAs of the previous tile's P V ----
+  // (1) masks and the row max; when the running max has to move, m and l move
+  // now and the factor for O is returned (O is rescaled only after all of the
+  // previous tile's P V has been added to it).
+  auto softmax_max = [&](f32x16 (&sc)[2], int kb, bool a0, bool a1, float& alpha) -> bool {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int k0 = kb + 32 * sub;
+      f32x16& acc = sc[sub];
+      if constexpr (SOFTCAP) {
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) acc[r2] = a.cap_log2 * tanh_f32(acc[r2] * a.scale_over_cap);
+      }
+      // masks only where the sub-tile crosses a frontier of some row of this
+      // wave (or is outside all of them)
+      const bool interior = (sub ? a1 : a0) && (a.window < 0 || k0 >= pw1 - a.window + 1) &&
+                            (!a.causal || k0 + 31 <= pw0) && (k0 + 31 < sp.valid);
+      if (!interior) {
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) {
+          const int j = k0 + 16 * (r2 >> 3) + 8 * h2 + (r2 & 7);
+          acc[r2] = (j < my_lo || j > my_hi) ? -INFINITY : acc[r2];
+        }
+      }
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2) bm = fmaxf(bm, acc[r2]);
+    }
+    // lane owns row n; lanes n and n+32 share the row
+    bm = fmaxf(bm, xor32(bm));
+    const float m_new = fmaxf(m_run, bm);
+    const bool need = (m_new - m_run) * c_l2 > kRescaleLog2;  // false while both are -inf
+    alpha = 1.0f;
+    const bool any = __any(need);
+    if (any) {
+      // a real branch: moving the running max is rare
+      asm volatile("" ::: "memory");
+      alpha = need ? fast_exp2((m_run - m_new) * c_l2) : 1.0f;
+      m_run = need ? m_new : m_run;
+      l_run *= alpha;
+    }
+    return any;
+  };
+  // (2) P = exp2(x - m) for keys 8 half .. 8 half + 7 of each row's two runs
+  // in sub-tile sub, packed to the input type; l += sum P
+  auto softmax_exp = [&](const f32x16& acc, int half, u32x4& pk) {
+    const float mb = m_run == -INFINITY ? 0.0f : m_run * c_l2;
+    float pv[8];
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2) {
+      pv[r2] = fast_exp2(fmaf(acc[8 * half + r2], c_l2, -mb));
+      l_run += pv[r2];
+    }
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) pk[q2] = pack2<IS_BF16>(pv[2 * q2], pv[2 * q2 + 1]);
+  };
+  auto rescale_o = [&](float alpha) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2) o[db][r2] *= alpha;
+  };
+
+  // ---- O^T += V^T P^T: four 16-key steps, the reads of the next step in
+  // flight during the MFMAs of the current one; consecutive MFMAs update
+  // different accumulators ----
+  auto pv = [&](uint32_t sbase, const u32x4 (&pb)[2][2], auto&& before, auto&& after) {
+    uint32_t vp[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vp[db] = sbase + vrd[db];
+    uint64_t vr[2][2 * DB];
+    auto vissue = [&](auto st_tag, uint64_t (&d)[2 * DB]) {
+      constexpr int ST = decltype(st_tag)::value;
+      if constexpr (DB == 4)
+        lds_issue_tr16x8<32 * D * ST, 32 * D * ST + 8 * D>(d, vp);
+      else
+        lds_issue_tr16x4<32 * D * ST, 32 * D * ST + 8 * D>(d, vp);
+    };
+    auto vstep = [&](auto st_tag) {
+      constexpr int ST = decltype(st_tag)::value;
+      uint64_t (&cur)[2 * DB] = vr[ST & 1];
+      if constexpr (ST + 1 < 4) {
+        vissue(std::integral_constant<int, ST + 1>{}, vr[(ST + 1) & 1]);
+        lds_wait_tr16<2 * DB>(cur);
+      } else {
+        lds_wait_tr16<0>(cur);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        o[db] = mma32<IS_BF16>(__builtin_bit_cast(u32x4, u64x2{cur[2 * db], cur[2 * db + 1]}),
+                               pb[ST >> 1][ST & 1], o[db]);
+    };
+    vissue(std::integral_constant<int, 0>{}, vr[0]);
+    before();
+    vstep(std::integral_constant<int, 0>{});
+    after(0);
+    vstep(std::integral_constant<int, 1>{});
+    after(1);
+    vstep(std::integral_constant<int, 2>{});
+    after(2);
+    vstep(std::integral_constant<int, 3>{});
+    after(3);
+  };
+
+  // ---- schedule: per tile, K Q^T (the next tile's loads riding along), the
+  // softmax, P V; then wait for the next tile and meet ----
   if (nblk > 0) dma_tile(kv_lo, 0);
   __builtin_amdgcn_s_waitcnt(0);  // Q registers and the first tile
   tile_barrier();
 
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0];
-  // per-lane byte offsets of the transposing V reads: rows 8 (g >> 1) + 4 r + j
-  // of each 16-key group, columns 16 (g & 1) + 4 c .. + 3 of each 32-column block
-  const int tg = lane >> 4, tj = (lane >> 2) & 3, tc = lane & 3;
+  f32x16 sc[2];
+  u32x4 pb[2][2];
   for (int it = 0; it < nblk; ++it) {
     const int kb = kv_lo + it * BN;
     const int buf = it & 1;
-    if (it + 1 < nblk) dma_tile(kb + BN, buf ^ 1);
-
-    // Sub-tiles (32 keys) this wave can see.  Interior tiles take the
-    // branch-free path (both active), so that LDS reads can be scheduled
-    // ahead of the MFMAs; frontier tiles take the general one.
-    const bool act0 = wrows > 0 && kb <= w_hi && kb + 31 >= w_lo;
-    const bool act1 = wrows > 0 && kb + 32 <= w_hi && kb + 63 >= w_lo;
-    auto tile = [&](auto full_tag) {
-      constexpr bool FULL = decltype(full_tag)::value;
-      const bool act[2] = {FULL || act0, FULL || act1};
-      // ---- S^T = K Q^T for both sub-tiles, the two chains interleaved ----
-      f32x16 s[2];
-      s[0] = f32x16{};
-      s[1] = f32x16{};
-      const uint32_t kbase = lds0 + buf * (2 * TILE * 2);
-      const uint32_t kp0 = kbase + 2 * kr0 * D;
-      const uint32_t kp1 = kbase + 2 * (32 + kr0) * D;
-      const int sw0 = k_swz<D>(kr0), sw1 = k_swz<D>(32 + kr0);
-      if constexpr (FULL) {
-        // both sub-tiles, two k-steps per batch of LDS reads
-        u32x4 kf[2][4];
-        auto issue = [&](int ks, u32x4 (&d)[4]) {
-          lds_issue_b128x4(d[0], d[1], d[2], d[3], kp0 + 16 * ((2 * ks + h2) ^ sw0),
-                           kp1 + 16 * ((2 * ks + h2) ^ sw1), kp0 + 16 * ((2 * ks + 2 + h2) ^ sw0),
-                           kp1 + 16 * ((2 * ks + 2 + h2) ^ sw1));
-        };
-        issue(0, kf[0]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ks += 2) {
-          u32x4 (&cur)[4] = kf[(ks >> 1) & 1];
-          if (ks + 2 < KS) {
-            issue(ks + 2, kf[((ks >> 1) + 1) & 1]);
-            lds_wait_b128x4<4>(cur[0], cur[1], cur[2], cur[3]);
-          } else {
-            lds_wait_b128x4<0>(cur[0], cur[1], cur[2], cur[3]);
-          }
-          s[0] = mma32<IS_BF16>(cur[0], qf[ks], s[0]);
-          s[1] = mma32<IS_BF16>(cur[1], qf[ks], s[1]);
-          s[0] = mma32<IS_BF16>(cur[2], qf[ks + 1], s[0]);
-          s[1] = mma32<IS_BF16>(cur[3], qf[ks + 1], s[1]);
-        }
-      } else {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          if (!act[sub]) continue;
-          const uint32_t kp = sub ? kp1 : kp0;
-          const int sw = sub ? sw1 : sw0;
-#pragma unroll
-          for (int ks = 0; ks < KS; ks += 2) {
-            u32x4 ka, kb2;
-            lds_b128x2(ka, kb2, kp + 16 * ((2 * ks + h2) ^ sw), kp + 16 * ((2 * ks + 2 + h2) ^ sw));
-            s[sub] = mma32<IS_BF16>(ka, qf[ks], s[sub]);
-            s[sub] = mma32<IS_BF16>(kb2, qf[ks + 1], s[sub]);
-          }
-        }
-      }
-      float bm = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (!act[sub]) continue;
-        const int k0 = kb + 32 * sub;
-        f32x16& acc = s[sub];
-        if constexpr (SOFTCAP) {
-#pragma unroll
-          for (int r2 = 0; r2 < 16; ++r2) acc[r2] = a.cap_log2 * tanh_f32(acc[r2] * a.scale_over_cap);
-        }
-        // masks only where the sub-tile crosses a frontier of some row of this wave
-        const bool interior = (a.window < 0 || k0 >= pw1 - a.window + 1) &&
-                              (!a.causal || k0 + 31 <= pw0) && (k0 + 31 < sp.valid);
-        if (!interior) {
-#pragma unroll
-          for (int r2 = 0; r2 < 16; ++r2) {
-            const int j = k0 + 16 * (r2 >> 3) + 8 * h2 + (r2 & 7);
-            acc[r2] = (j < my_lo || j > my_hi) ? -INFINITY : acc[r2];
-          }
-        }
-#pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) bm = fmaxf(bm, acc[r2]);
-      }
-
-      // ---- online softmax (lane owns row n; lanes n and n+32 share the row) ----
-      bm = fmaxf(bm, xor32(bm));
-      const float m_new = fmaxf(m_run, bm);
-      const bool need = (m_new - m_run) * c_l2 > kRescaleLog2;  // false while both are -inf
-      if (__any(need)) {
-        const float alpha = need ? fast_exp2((m_run - m_new) * c_l2) : 1.0f;
-        m_run = need ? m_new : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r2 = 0; r2 < 16; ++r2) o[db][r2] *= alpha;
-      }
-      const float mb = m_run == -INFINITY ? 0.0f : m_run * c_l2;
-      u32x4 pb[2][2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (!act[sub]) continue;
-        float pv[16];
-#pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) {
-          pv[r2] = fast_exp2(fmaf(s[sub][r2], c_l2, -mb));
-          l_run += pv[r2];
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2)
-            pb[sub][t][q2] = pack2<IS_BF16>(pv[8 * t + 2 * q2], pv[8 * t + 2 * q2 + 1]);
-      }
-
-      // ---- O^T += V^T P^T: consecutive MFMAs update different accumulators ----
-      if constexpr (FULL && DB == 4) {
-        // the four 16-key steps, the reads of the next one in flight during
-        // the MFMAs of the current one
-        uint64_t vr[2][8];
-        auto vaddr = [&](int st, uint32_t (&pa)[8]) {
-          const int sub = st >> 1, t = st & 1;
-          const int key0 = 32 * sub + 16 * t + 8 * (tg >> 1) + tj;
-          const uint32_t vrow0 = lds0 + buf * (2 * TILE * 2) + 2 * TILE + 2 * D * key0;
-          const uint32_t vrow1 = vrow0 + 2 * D * 4;
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int chunk = 4 * db + 2 * (tg & 1) + (tc >> 1);
-            pa[2 * db] = vrow0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
-            pa[2 * db + 1] = vrow1 + 16 * (chunk ^ vrow_swz<D>(key0 + 4)) + 8 * (tc & 1);
-          }
-        };
-        {
-          uint32_t pa[8];
-          vaddr(0, pa);
-          lds_issue_tr16x8(vr[0], pa);
-        }
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          uint64_t (&cur)[8] = vr[st & 1];
-          if (st + 1 < 4) {
-            uint32_t pa[8];
-            vaddr(st + 1, pa);
-            lds_issue_tr16x8(vr[(st + 1) & 1], pa);
-            lds_wait_tr16x8<8>(cur);
-          } else {
-            lds_wait_tr16x8<0>(cur);
-          }
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-            o[db] = mma32<IS_BF16>(__builtin_bit_cast(u32x4, u64x2{cur[2 * db], cur[2 * db + 1]}),
-                                   pb[st >> 1][st & 1], o[db]);
-        }
-        return;
-      }
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (!act[sub]) continue;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int key0 = 32 * sub + 16 * t + 8 * (tg >> 1) + tj;  // + 4 r
-          const uint32_t vrow0 = lds0 + buf * (2 * TILE * 2) + 2 * TILE + 2 * D * key0;
-          const uint32_t vrow1 = vrow0 + 2 * D * 4;
-          if constexpr (DB == 4) {
-            uint32_t pa[8];
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              const int chunk = 4 * db + 2 * (tg & 1) + (tc >> 1);
-              pa[2 * db] = vrow0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
-              pa[2 * db + 1] = vrow1 + 16 * (chunk ^ vrow_swz<D>(key0 + 4)) + 8 * (tc & 1);
-            }
-            u32x4 vf[4];
-            lds_tr16x8(vf, pa);
-#pragma unroll
-            for (int db = 0; db < 4; ++db) o[db] = mma32<IS_BF16>(vf[db], pb[sub][t], o[db]);
-          } else {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const int chunk = 4 * db + 2 * (tg & 1) + (tc >> 1);
-              const uint32_t off0 = 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
-              const uint32_t off1 = 16 * (chunk ^ vrow_swz<D>(key0 + 4)) + 8 * (tc & 1);
-              const u32x4 vf = lds_tr16x2(vrow0 + off0, vrow1 + off1);
-              o[db] = mma32<IS_BF16>(vf, pb[sub][t], o[db]);
-            }
-          }
-        }
-      }
+    const uint32_t sbase = lds0 + buf * kStage;
+    // The next tile's loads are spread over the K operand batches (or issued
+    // at once by a wave with nothing to compute here): a wave that issued all
+    // of them back to back would stall behind the other waves' loads.
+    const bool next = it + 1 < nblk;
+    auto dma_at = [&](int i) {
+      if (next) dma_part(kb + BN, buf ^ 1, i);
     };
-    if (act0 && act1)
-      tile(std::true_type{});
-    else if (act0 || act1)
-      tile(std::false_type{});
-
-    // this wave's DMA loads of the next tile have landed; after the barrier
-    // every wave's have, and nobody reads this tile's stage any more
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    bool a0, a1;
+    active(kb, a0, a1);
+    if (a0 || a1) {
+      qk(sbase, sc, dma_at);
+      float alpha;
+      if (softmax_max(sc, kb, a0, a1, alpha)) rescale_o(alpha);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) softmax_exp(sc[q >> 1], q & 1, pb[q >> 1][q & 1]);
+      pv(sbase, pb, [] {}, [](int) {});
+    } else if (next) {
+      dma_tile(kb + BN, buf ^ 1);
+    }
+    // this wave's loads of the next tile have landed; after the barrier every
+    // wave's have, and nobody reads this tile's stage any more
+    wait_vm<0>();
     tile_barrier();
   }
 
@@ -538,14 +525,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 template <bool IS_BF16, int D>
 hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
-  const int nrb = (a.Lq + BM - 1) / BM;
-  const int items = a.B * a.Hq * nrb;
+  // heads per workgroup: the largest power of two that divides G, at most 8
+  const int hw = std::min(a.G & -a.G, kWaves);
+  const int rpw = 32 * (kWaves / hw);
+  const int nrb = (a.Lq + rpw - 1) / rpw;
+  const int items = a.B * a.Hkv * (a.G / hw) * nrb;
   const int per_xcd = (items + 7) / 8;
-  dim3 grid(8 * per_xcd), block(256);
+  dim3 grid(8 * per_xcd), block(64 * kWaves);
   if (softcap)
-    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, true>), grid, block, 0, stream, a, nrb, items, per_xcd);
+    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, true>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false>), grid, block, 0, stream, a, nrb, items, per_xcd);
+    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
   return hipGetLastError();
 }
 
