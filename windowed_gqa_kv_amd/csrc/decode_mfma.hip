@@ -285,6 +285,15 @@ __device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt,
 #pragma unroll
         for (int q = 0; q < QPL; ++q) v[e][q] = *reinterpret_cast<const f32x4*>(p + rr * D + 4 * (c * QPL + q));
       }
+      // The batch's loads are all in flight before any of them is used: left
+      // alone, the compiler sinks them below the branch and issues them one
+      // round trip at a time.
+#pragma unroll
+      for (int e = 0; e < NB; ++e) {
+        asm volatile("" ::"v"(mv[e]), "v"(lv[e]));
+#pragma unroll
+        for (int q = 0; q < QPL; ++q) asm volatile("" ::"v"(v[e][q]));
+      }
       float mb = M;
 #pragma unroll
       for (int e = 0; e < NB; ++e) {
