@@ -53,6 +53,7 @@ constexpr int kWaves = 4;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kMaxTiles = 2048;       // row tiles per call on this path
 constexpr int kMaxGrid = 2048;        // workgroups per launch (upper bound)
+constexpr int kCachedTiles = 160;     // tiles whose lengths the setup keeps in LDS
 
 // LDS staging of one wave: kStages units of K and V in flight, 16 KB per
 // wave for head sizes up to 128 (two workgroups share a CU, so one wave's
@@ -362,6 +363,9 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   __shared__ int pre[kMaxTiles + 2];  // unit prefix sum over tiles (then workgroups per tile)
   __shared__ int wsum[4];
   __shared__ int flag[256];
+  // (q_off, valid, lo, hi) of each tile, kept by the setup when there are
+  // few tiles, so that starting a piece needs no memory round trip
+  __shared__ int4 tcache[kCachedTiles];
   float (*merge_lds)[MERGE * 64] = reinterpret_cast<float (*)[MERGE * 64]>(&ring[0]);
 
   const int tid = threadIdx.x;
@@ -390,7 +394,12 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       __syncthreads();
     }
   };
-  block_scan(pre, [&](int t) { return units_of(make_tile(a, rows, nrt, t)); });
+  const bool cached = T <= kCachedTiles;
+  block_scan(pre, [&](int t) {
+    const Tile x = make_tile(a, rows, nrt, t);
+    if (cached) tcache[t] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
+    return units_of(x);
+  });
   const int U = pre[T];
 
   // tiles nobody streams (no allowed key for any of their rows) output zeros
@@ -494,7 +503,22 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     const int ub = min(uend, pre[t + 1]) - pre[t];
     u = pre[t] + ub;
     t_last = t;
-    const Tile x = make_tile(a, rows, nrt, t);
+    Tile x;
+    if (cached) {
+      // the same values make_tile computes, without loading the lengths again
+      const int4 c = tcache[t];
+      x.bg = t / nrt;
+      x.rt = t - x.bg * nrt;
+      x.b = x.bg / a.Hkv;
+      x.g = x.bg - x.b * a.Hkv;
+      x.sp.q_off = c.x;
+      x.sp.valid = c.y;
+      x.lo = c.z;
+      x.hi = c.w;
+      x.rows_tile = min(kRowsPerTile, rows - kRowsPerTile * x.rt);
+    } else {
+      x = make_tile(a, rows, nrt, t);
+    }
     const int c_lo = x.lo + kSub * ua;
     const int c_hi = min(x.hi, x.lo + kSub * ub - 1);
 
