@@ -54,6 +54,7 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr int kMaxTiles = 2048;       // row tiles per call on this path
 constexpr int kMaxGrid = 2048;        // workgroups per launch (upper bound)
 constexpr int kCachedTiles = 160;     // tiles whose lengths the setup keeps in LDS
+constexpr int kNonTemporal = 2;       // cache-policy bits of a load: nt (gfx950)
 
 // LDS staging of one wave: kStages units of K and V in flight, 16 KB per
 // wave for head sizes up to 128 (two workgroups share a CU, so one wave's
@@ -566,10 +567,11 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
         const int key = pos / RG::kSlots;
         const int cc = (pos % RG::kSlots) ^ swz<D>(key);  // the global chunk stored there
         const int row = min(kb + key, c_hi);
+        // K/V bytes are read once per call: non-temporal (streaming) loads
         __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)row * a.k_ss + 8 * cc),
-                                         (lds_void*)(kdst + 1024 * i), 16, 0, 0);
+                                         (lds_void*)(kdst + 1024 * i), 16, 0, kNonTemporal);
         __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)row * a.v_ss + 8 * cc),
-                                         (lds_void*)(vdst + 1024 * i), 16, 0, 0);
+                                         (lds_void*)(vdst + 1024 * i), 16, 0, kNonTemporal);
       }
     };
     const int npro = min(nw, S);
