@@ -234,42 +234,53 @@ __device__ __forceinline__ int mul_div(int x, int i, int n) {
   return q * i + (r * i) / n;
 }
 
+// LSE-combine of two partial states (max M in log2 units, sum Ls, acc) that
+// share a lane layout; an empty state has M = -inf and contributes nothing.
+template <int QPL>
+__device__ __forceinline__ void lse_combine(float& M, float& Ls, f32x4 (&acc)[QPL], float Mo, float Lo,
+                                            const float (&ao)[QPL * 4]) {
+  const float Mn = fmaxf(M, Mo);
+  const float fa = Mn == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+  const float fb = Mn == -INFINITY ? 0.0f : fast_exp2(Mo - Mn);
+  Ls = Ls * fa + Lo * fb;
+#pragma unroll
+  for (int q = 0; q < QPL; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[q][e] = acc[q][e] * fa + ao[4 * q + e] * fb;
+  M = Mn;
+}
+
 // Merge of one row tile's split partials by one wave (no barriers, no LDS):
 // log-sum-exp over the splits, sink folded into the denominator, normalised,
 // narrowed with round-to-nearest-even and stored.  Split x of the tile is the
 // partial at gpart + x * PART (acc [16][D], then 16 maxima in log2 units,
-// then 16 sums).  Lanes are laid out as (row, split group, chunk of 8 output
-// quads): each lane merges its split group's partials for its chunk, batches
-// of NB splits in flight at once, and the split groups of a row are then
-// combined with shuffles.
-template <bool IS_BF16, int D>
-__device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt, int tt,
-                                           const float* __restrict__ gpart, int nvalid, int lane) {
+// then 16 sums).  The tile's rows are padded to Rp = 2^lrp and each row gets
+// 64 / Rp lanes; a lane owns QPL output quads of its row (a chunk) and merges
+// them over its splits, NB splits in flight at once.  Only when a row has
+// more lanes than quads (one or two rows) do several lanes share a chunk as
+// split groups, combined with shuffles at the end.
+template <bool IS_BF16, int D, int QPL>
+__device__ __forceinline__ void merge_tile_q(const AttnArgs& a, int lrp, int R, int rt, int xb, int xg,
+                                             const float* __restrict__ gpart, int nvalid, int lane) {
   constexpr int PART = kRowsPerTile * D + 2 * kRowsPerTile;
-  constexpr int Q4 = D / 4;        // output quads per row
-  constexpr int QPL = 8;           // quads per lane and pass
-  constexpr int NC = Q4 / QPL;     // chunks per row
-  constexpr int NB = 4;            // splits per lane in flight
+  constexpr int Q4 = D / 4;  // output quads per row
+  constexpr int NC = Q4 / QPL;  // chunks per row
+  // splits per lane in flight: 64 loaded quads per lane, or 128 at D = 256,
+  // whose kernel runs one workgroup per CU and has the registers to spare
+  constexpr int NB = (D >= 256 ? 32 : 16) / QPL;
   static_assert(Q4 % QPL == 0, "whole chunks");
-  // the other workgroups' write-through stores were complete before their
-  // arrivals, which this workgroup has seen: acquire once before reading
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // the tile's coordinates (no lengths needed here)
-  const int bg = tt / nrt, rt = tt - bg * nrt;
-  const int xb = bg / a.Hkv, xg = bg - xb * a.Hkv;
-  const int R = min(kRowsPerTile, rows - kRowsPerTile * rt);
-  const int lrp = R <= 1 ? 0 : (R <= 2 ? 1 : (R <= 4 ? 2 : (R <= 8 ? 3 : 4)));  // log2 of padded rows
   const int L = 64 >> lrp;           // lanes per row
   const int r = lane >> (6 - lrp);
   const int sub = lane & (L - 1);
   const int CL = min(L, NC);         // lanes of a row on distinct chunks
-  const int SG = L / CL;             // split groups per row
+  const int SG = L / CL;             // split groups per row (> 1 only with QPL == 1)
   const int sg = sub / CL;
   const bool row_ok = r < R;
   const int rr = row_ok ? r : 0;
   const int row = kRowsPerTile * rt + rr;
   const int h = xg * a.G + row % a.G;
   const float sink = a.use_sink ? sink_log2(a, h) : 0.0f;
+  // NC / CL passes, the same number in every lane and wave
   for (int c = sub % CL; c < NC; c += CL) {
     float M = -INFINITY, Ls = 0.0f;
     f32x4 acc[QPL];
@@ -320,15 +331,12 @@ __device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt,
     for (int off = CL; off < L; off <<= 1) {
       const float Mo = __shfl_xor(M, off, 64);
       const float Lo = __shfl_xor(Ls, off, 64);
-      const float Mn = fmaxf(M, Mo);
-      const float fa = Mn == -INFINITY ? 0.0f : fast_exp2(M - Mn);
-      const float fb = Mn == -INFINITY ? 0.0f : fast_exp2(Mo - Mn);
-      Ls = Ls * fa + Lo * fb;
+      float ao[QPL * 4];
 #pragma unroll
       for (int q = 0; q < QPL; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[q][e] = acc[q][e] * fa + __shfl_xor(acc[q][e], off, 64) * fb;
-      M = Mn;
+        for (int e = 0; e < 4; ++e) ao[4 * q + e] = __shfl_xor(acc[q][e], off, 64);
+      lse_combine<QPL>(M, Ls, acc, Mo, Lo, ao);
     }
     if (row_ok && sg == 0) {
       float fac;
@@ -345,6 +353,30 @@ __device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt,
       for (int q = 0; q < QPL; ++q) store_row4<IS_BF16, D>(a, xb, h, row / a.G, 4 * (c * QPL + q), acc[q] * fac);
     }
   }
+}
+
+// Quads per lane for a tile of R rows: the row's lanes (64 / Rp) cover its
+// D / 4 output quads once where they can, at most 8 quads per lane.
+template <bool IS_BF16, int D>
+__device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt, int tt,
+                                           const float* __restrict__ gpart, int nvalid, int lane) {
+  // the other workgroups' write-through stores were complete before their
+  // arrivals, which this workgroup has seen: acquire once before reading
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // the tile's coordinates (no lengths needed here)
+  const int bg = tt / nrt, rt = tt - bg * nrt;
+  const int xb = bg / a.Hkv, xg = bg - xb * a.Hkv;
+  const int R = min(kRowsPerTile, rows - kRowsPerTile * rt);
+  const int lrp = R <= 1 ? 0 : (R <= 2 ? 1 : (R <= 4 ? 2 : (R <= 8 ? 3 : 4)));  // log2 of padded rows
+  const int qpl = ((D / 4) << lrp) / 64;  // quads of a row / lanes of a row
+  if (qpl <= 1)
+    merge_tile_q<IS_BF16, D, 1>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
+  else if (qpl == 2)
+    merge_tile_q<IS_BF16, D, 2>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
+  else if (qpl == 4)
+    merge_tile_q<IS_BF16, D, 4>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
+  else
+    merge_tile_q<IS_BF16, D, 8>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
 }
 
 template <bool IS_BF16, int D, bool SOFTCAP>
