@@ -428,12 +428,34 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     }
   };
   const bool cached = T <= kCachedTiles;
-  block_scan(pre, [&](int t) {
-    const Tile x = make_tile(a, rows, nrt, t);
-    if (cached) tcache[t] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
-    return units_of(x);
-  });
-  const int U = pre[T];
+  int U;
+  if (T <= 64) {
+    // one tile per lane: every wave scans in registers on its own (no
+    // barriers inside the scan); wave 0 publishes the prefix sums
+    Tile x{};
+    int ut = 0;
+    if (lane < T) {
+      x = make_tile(a, rows, nrt, lane);
+      ut = units_of(x);
+    }
+    const int incl = wave_incl_scan(ut, lane);
+    U = __builtin_amdgcn_readlane(incl, 63);
+    if (w == 0) {
+      if (lane == 0) pre[0] = 0;
+      if (lane < T) {
+        pre[lane + 1] = incl;
+        if (cached) tcache[lane] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
+      }
+    }
+    __syncthreads();
+  } else {
+    block_scan(pre, [&](int t) {
+      const Tile x = make_tile(a, rows, nrt, t);
+      if (cached) tcache[t] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
+      return units_of(x);
+    });
+    U = pre[T];
+  }
 
   // tiles nobody streams (no allowed key for any of their rows) output zeros
   for (int t = k; t < T; t += G) {
