@@ -78,7 +78,7 @@ __device__ __forceinline__ int key_of_m(int m) {
 // XOR swizzle of the 16-byte chunks of K row r: the 16 rows one operand read
 // touches per 16 lanes land on 16 different bank groups.
 template <int D>
-__device__ __forceinline__ int k_swz(int r) {
+__host__ __device__ constexpr int k_swz(int r) {
   if constexpr (D == 128)
     return r & 15;
   else
@@ -87,7 +87,7 @@ __device__ __forceinline__ int k_swz(int r) {
 // V tile rows (row-major, 16-byte chunks XOR-swizzled by key): the
 // transposing reads of the P*V operand then hit every bank equally.
 template <int D>
-__device__ __forceinline__ int vrow_swz(int key) {
+__host__ __device__ constexpr int vrow_swz(int key) {
   if constexpr (D == 128)
     return 4 * (key & 3);
   else
@@ -118,6 +118,21 @@ __device__ __forceinline__ void lds_issue_b128x4(u32x4& a0, u32x4& a1, u32x4& a2
       "ds_read_b128 %3, %7"
       : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
       : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+      : "memory");
+}
+// Four K operand reads: two k-steps (addresses p0, p1) of both 32-key
+// sub-tiles (immediate offsets OFF and OFF + SUB).
+template <int OFF, int SUB>
+__device__ __forceinline__ void lds_issue_b128x4_at(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, uint32_t p0,
+                                                    uint32_t p1) {
+  static_assert(OFF >= 0 && OFF + SUB <= 65535, "LDS immediate offset range");
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%6\n\t"
+      "ds_read_b128 %1, %4 offset:%7\n\t"
+      "ds_read_b128 %2, %5 offset:%6\n\t"
+      "ds_read_b128 %3, %5 offset:%7"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+      : "v"(p0), "v"(p1), "n"(OFF), "n"(OFF + SUB)
       : "memory");
 }
 template <int N>
@@ -163,6 +178,16 @@ __device__ __forceinline__ void lds_wait_tr16(uint64_t (&r)[8]) {
 template <int N>
 __device__ __forceinline__ void lds_wait_tr16(uint64_t (&r)[4]) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N) : "memory");
+}
+// One wave-wide LDS DMA load (16 bytes per lane, 1 KB in all) from the
+// uniform base sbase plus this lane's 32-bit byte offset voff, to the LDS
+// bytes at lds_addr + 16 * lane.  The scalar-base form keeps the tile's base
+// address off the vector ALU.  The compiler does not see it as a memory
+// load: the callers wait for it with explicit vmcnt waits.
+__device__ __forceinline__ void dma_saddr(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  // M0 (the LDS destination) is an input operand, so the compiler sets it
+  // and knows its value afterwards
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 // Barrier for waves whose only LDS accesses are the inline-assembly ones:
 // wait for this wave's LDS operations, then meet.  (A fenced barrier would
@@ -276,8 +301,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     if (kb + BN - 1 <= kv_hi) {
       const char* kbase = reinterpret_cast<const char*>(Kg) + kb * krow_b;
       const char* vbase = reinterpret_cast<const char*>(Vg) + kb * vrow_b;
-      __builtin_amdgcn_global_load_lds((global_void*)(kbase + koff[i]), (lds_void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void*)(vbase + voff[i]), (lds_void*)vdst, 16, 0, 0);
+      dma_saddr(kbase, koff[i], (uint32_t)(uintptr_t)(lds_void*)kdst);
+      dma_saddr(vbase, voff[i], (uint32_t)(uintptr_t)(lds_void*)vdst);
     } else {
       const int r = RPI * (NDMA * w + i) + lane / CPR, slot = lane % CPR;
       const int j = min(kb + r, kv_hi);
@@ -297,7 +322,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int kr0 = key_of_m(n);                        // this lane's K row in a sub-tile
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0];
-  constexpr uint32_t kStage = 2 * TILE * 2;  // bytes of one K + V stage
+  constexpr int kStage = 2 * TILE * 2;  // bytes of one K + V stage
+  constexpr int kSubBytes = 2 * 32 * D;  // bytes of one 32-key sub-tile of K
+  // Per-lane LDS addresses of the K operand reads of stage 0, sub-tile 0, one
+  // per k-step (chunk 2 ks + h2 of row kr0); the other sub-tile and stage are
+  // immediate offsets, since row 32 + r has the same swizzle as row r.
+  static_assert(k_swz<D>(32) == k_swz<D>(0) && k_swz<D>(33) == k_swz<D>(1) && k_swz<D>(63) == k_swz<D>(31),
+                "sub-tiles share the K swizzle");
+  uint32_t kra[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kra[ks] = lds0 + 2 * kr0 * D + 16 * ((2 * ks + h2) ^ k_swz<D>(kr0));
   // Per-lane byte offsets (within a stage) of the transposing V reads of
   // 16-key step 0: rows 8 (g >> 1) + j (+ 4) of the step, columns
   // 16 (g & 1) + 4 c .. + 3 of each 32-column block.  Step st adds 32 D st
@@ -312,6 +346,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       vrd[db] = 2 * TILE + 2 * D * key0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
     }
   }
+  uint32_t vra[DB];  // the same as LDS addresses of stage 0; the stage is an immediate offset
+#pragma unroll
+  for (int db = 0; db < DB; ++db) vra[db] = lds0 + vrd[db];
 
   // Sub-tiles (32 keys) of the tile at kb that this wave can see; a tile with
   // at least one is computed whole, and a sub-tile outside every row's band
@@ -323,17 +360,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   // ---- S^T = K Q^T for both sub-tiles, two k-steps per batch of reads; the
   // DMA pairs of a later tile ride along, one per batch ----
-  auto qk = [&](uint32_t sbase, f32x16 (&sc)[2], auto&& dma_at) {
+  auto qk = [&](auto st_tag, f32x16 (&sc)[2], auto&& dma_at) {
+    constexpr int ST = decltype(st_tag)::value;
     sc[0] = f32x16{};
     sc[1] = f32x16{};
-    const uint32_t kp0 = sbase + 2 * kr0 * D;
-    const uint32_t kp1 = sbase + 2 * (32 + kr0) * D;
-    const int sw0 = k_swz<D>(kr0), sw1 = k_swz<D>(32 + kr0);
     u32x4 kf[2][4];
     auto issue = [&](int ks, u32x4 (&d)[4]) {
-      lds_issue_b128x4(d[0], d[1], d[2], d[3], kp0 + 16 * ((2 * ks + h2) ^ sw0),
-                       kp1 + 16 * ((2 * ks + h2) ^ sw1), kp0 + 16 * ((2 * ks + 2 + h2) ^ sw0),
-                       kp1 + 16 * ((2 * ks + 2 + h2) ^ sw1));
+      lds_issue_b128x4_at<ST * kStage, kSubBytes>(d[0], d[1], d[2], d[3], kra[ks], kra[ks + 1]);
     };
     issue(0, kf[0]);
 #pragma unroll
@@ -416,22 +449,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r2 = 0; r2 < 16; ++r2) o[db][r2] *= alpha;
+    // the scaled accumulators pass through an asm statement that cannot be
+    // speculated, so the (rare) multiplies stay behind the branch instead of
+    // being hoisted out of it as o * (cond ? alpha : 1)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(o[db]));
   };
 
   // ---- O^T += V^T P^T: four 16-key steps, the reads of the next step in
   // flight during the MFMAs of the current one; consecutive MFMAs update
   // different accumulators ----
-  auto pv = [&](uint32_t sbase, const u32x4 (&pb)[2][2], auto&& before, auto&& after) {
-    uint32_t vp[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) vp[db] = sbase + vrd[db];
+  auto pv = [&](auto stage_tag, const u32x4 (&pb)[2][2], auto&& before, auto&& after) {
+    constexpr int SO = decltype(stage_tag)::value * kStage;
     uint64_t vr[2][2 * DB];
     auto vissue = [&](auto st_tag, uint64_t (&d)[2 * DB]) {
       constexpr int ST = decltype(st_tag)::value;
       if constexpr (DB == 4)
-        lds_issue_tr16x8<32 * D * ST, 32 * D * ST + 8 * D>(d, vp);
+        lds_issue_tr16x8<SO + 32 * D * ST, SO + 32 * D * ST + 8 * D>(d, vra);
       else
-        lds_issue_tr16x4<32 * D * ST, 32 * D * ST + 8 * D>(d, vp);
+        lds_issue_tr16x4<SO + 32 * D * ST, SO + 32 * D * ST + 8 * D>(d, vra);
     };
     auto vstep = [&](auto st_tag) {
       constexpr int ST = decltype(st_tag)::value;
@@ -467,33 +503,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   f32x16 sc[2];
   u32x4 pb[2][2];
-  for (int it = 0; it < nblk; ++it) {
+  // One tile; its stage (it & 1) is a compile-time constant, so that every
+  // LDS address of the tile is a per-lane register plus an immediate.
+  auto tile = [&](int it, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
     const int kb = kv_lo + it * BN;
-    const int buf = it & 1;
-    const uint32_t sbase = lds0 + buf * kStage;
     // The next tile's loads are spread over the K operand batches (or issued
     // at once by a wave with nothing to compute here): a wave that issued all
     // of them back to back would stall behind the other waves' loads.
     const bool next = it + 1 < nblk;
     auto dma_at = [&](int i) {
-      if (next) dma_part(kb + BN, buf ^ 1, i);
+      if (next) dma_part(kb + BN, ST ^ 1, i);
     };
     bool a0, a1;
     active(kb, a0, a1);
     if (a0 || a1) {
-      qk(sbase, sc, dma_at);
+      qk(stage_tag, sc, dma_at);
       float alpha;
       if (softmax_max(sc, kb, a0, a1, alpha)) rescale_o(alpha);
 #pragma unroll
       for (int q = 0; q < 4; ++q) softmax_exp(sc[q >> 1], q & 1, pb[q >> 1][q & 1]);
-      pv(sbase, pb, [] {}, [](int) {});
+      pv(stage_tag, pb, [] {}, [](int) {});
     } else if (next) {
-      dma_tile(kb + BN, buf ^ 1);
+      dma_tile(kb + BN, ST ^ 1);
     }
     // this wave's loads of the next tile have landed; after the barrier every
     // wave's have, and nobody reads this tile's stage any more
     wait_vm<0>();
     tile_barrier();
+  };
+  for (int it = 0; it < nblk; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < nblk) tile(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: fold the sink, normalize, narrow, store ----
