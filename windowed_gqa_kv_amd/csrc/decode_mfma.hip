@@ -429,7 +429,12 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   };
   const bool cached = T <= kCachedTiles;
   int U;
-  if (T <= 64) {
+  // With at most 64 row tiles, lane t of every wave keeps tile t's unit count
+  // and prefix sums in registers, and the split below works on them without
+  // LDS round trips (the same values every wave; wave 0 publishes them).
+  const bool small = T <= 64;
+  int my_ut = 0, my_pre = 0, my_nt = 0, my_pren = 0;
+  if (small) {
     // one tile per lane: every wave scans in registers on its own (no
     // barriers inside the scan); wave 0 publishes the prefix sums
     Tile x{};
@@ -440,6 +445,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     }
     const int incl = wave_incl_scan(ut, lane);
     U = __builtin_amdgcn_readlane(incl, 63);
+    my_ut = ut;
+    my_pre = incl - ut;
     if (w == 0) {
       if (lane == 0) pre[0] = 0;
       if (lane < T) {
@@ -485,12 +492,27 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       int c = 0;
-      for (int t = lane; t < T; t += 64) c += (pre[t + 1] - pre[t] + mid - 1) / mid;
+      if (small)
+        c = (my_ut + mid - 1) / mid;  // 0 in lanes past the last tile
+      else
+        for (int t = lane; t < T; t += 64) c += (pre[t + 1] - pre[t] + mid - 1) / mid;
       if (wave_sum(c, lane) <= G) hi = mid; else lo = mid + 1;
     }
     const int L = lo;
-    block_scan(pren, [&](int t) { return (pre[t + 1] - pre[t] + L - 1) / L; });
-    Gs = pren[T];
+    if (small) {
+      my_nt = (my_ut + L - 1) / L;
+      const int nincl = wave_incl_scan(my_nt, lane);
+      my_pren = nincl - my_nt;
+      Gs = __builtin_amdgcn_readlane(nincl, 63);
+      if (w == 0) {
+        if (lane == 0) pren[0] = 0;
+        if (lane < T) pren[lane + 1] = nincl;
+      }
+      __syncthreads();  // pren[] is read by the arrivals at the end
+    } else {
+      block_scan(pren, [&](int t) { return (pre[t + 1] - pre[t] + L - 1) / L; });
+      Gs = pren[T];
+    }
   } else {
     Gs = min(G, U);
   }
@@ -507,7 +529,16 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   };
 
   int ustart, uend, t_first;
-  if (aligned) {
+  if (aligned && small) {
+    // the largest t with pren[t] <= k (a prefix of the lanes; never an empty tile)
+    t_first = 63 - __builtin_clzll(__ballot(lane < T && my_pren <= k));
+    const int ut = __builtin_amdgcn_readlane(my_ut, t_first);
+    const int pt = __builtin_amdgcn_readlane(my_pre, t_first);
+    const int n = __builtin_amdgcn_readlane(my_nt, t_first);
+    const int i = k - __builtin_amdgcn_readlane(my_pren, t_first);
+    ustart = pt + mul_div(ut, i, n);
+    uend = pt + mul_div(ut, i + 1, n);
+  } else if (aligned) {
     int lo = 0, hi = T;  // invariant: pren[lo] <= k < pren[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
