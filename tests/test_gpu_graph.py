@@ -55,3 +55,35 @@ def test_decode_step_graph_replays(gpu, w):
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e), f"replay {rep}"
         assert torch.equal(other, out_e), f"eager call after replay {rep}"
+
+
+def test_decode_steps_chained_in_one_graph(gpu):
+    """Two steps (two caches) captured back to back in one graph, as the
+    benchmark replays them: every replay gives each step's eager result."""
+    w = CASES[0]
+    d = generate(w)
+    plan = make_plan(w)
+    caches = [(d["k_cache"].cuda(), d["v_cache"].cuda()) for _ in range(2)]
+    seq, q = d["seqlens_k"].cuda(), d["q"].cuda()
+    kn, vn = d["k_new"].cuda(), d["v_new"].cuda()
+    ws = torch.zeros(plan.workspace_size(), dtype=torch.uint8, device="cuda")
+    out_e = torch.empty_like(q)
+    plan.append_kv(kn, vn, *caches[0], seq)
+    plan.decode(q, *caches[0], seq, out_e, workspace=ws)
+    torch.cuda.synchronize()
+    compare(out_e, oracle_decode(w, d), w.dtype, f"eager {w}")
+    outs = [torch.empty_like(q) for _ in range(2)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(2):
+            plan.append_kv(kn, vn, *caches[i], seq)
+            plan.decode(q, *caches[i], seq, outs[i], workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], out_e), f"replay {rep}, step {i}"
