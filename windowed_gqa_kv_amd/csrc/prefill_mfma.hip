@@ -109,17 +109,6 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 // consumed whole, as MFMA operands (single elements of a vector-typed
 // inline-asm result are mis-assigned to sub-registers by this compiler); the
 // 64-bit halves of a V operand come back as scalars.
-__device__ __forceinline__ void lds_issue_b128x4(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, uint32_t p0,
-                                                 uint32_t p1, uint32_t p2, uint32_t p3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7"
-      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
-      : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
-      : "memory");
-}
 // Four K operand reads: two k-steps (addresses p0, p1) of both 32-key
 // sub-tiles (immediate offsets OFF and OFF + SUB).
 template <int OFF, int SUB>
