@@ -612,7 +612,6 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     const int my_r = kRowsPerTile * x.rt + n;
     const bool row_ok = n < x.rows_tile;
     const int my_t = row_ok ? my_r / a.G : 0;
-    const int my_h = x.g * a.G + (row_ok ? my_r % a.G : 0);
     const int my_p = x.sp.q_off + my_t;
     const int lo_eff = max(row_lo(a, my_p), c_lo);
     const int hi_eff = min(row_hi(a, my_p, x.sp.valid), c_hi);
