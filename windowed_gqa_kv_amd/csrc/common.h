@@ -159,5 +159,13 @@ __device__ __forceinline__ float xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
+// The value of lane l ^ 16 (v_permlane16_swap exchanges the odd 16-lane rows
+// of one operand with the even rows of the other; with both operands x, a
+// lane in an odd row finds its partner in the first result, one in an even
+// row in the second).
+__device__ __forceinline__ float xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
 
 }  // namespace gqa

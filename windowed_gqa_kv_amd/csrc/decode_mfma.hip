@@ -701,8 +701,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       }
       // online softmax: lanes n, n+16, n+32, n+48 share row n
       float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      bm = fmaxf(bm, xor16(bm));
+      bm = fmaxf(bm, xor32(bm));
       const float m_new = fmaxf(m_run, bm);
       const bool need = (m_new - m_run) * c_l2 > kRescaleLog2;
       if (__any(need)) {
@@ -768,8 +768,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     __syncthreads();
     if (w == 0) {
       take(0);
-      float l_row = l_run + __shfl_xor(l_run, 16, 64);
-      l_row += __shfl_xor(l_row, 32, 64);
+      float l_row = l_run + xor16(l_run);
+      l_row += xor32(l_row);
       if (row_ok) {
         float* p = part + (int64_t)(k + t) * PART;  // slot k + t: unique per piece
 #pragma unroll
