@@ -8,6 +8,7 @@ nothing from the product path.
 
 ``attention``  plain materialized float64 attention (NumPy), the definition.
 ``brute``      the same definition with scalar Python loops, for tiny shapes.
+``rotary``     rotary position embedding of Q and of K before it enters the cache.
 """
 
 from .materialized import (  # noqa: F401
@@ -20,3 +21,4 @@ from .materialized import (  # noqa: F401
     softcap_fn,
 )
 from . import brute  # noqa: F401
+from . import rotary  # noqa: F401

@@ -426,6 +426,11 @@ def _golden_cases():
 
 @pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
 def test_hand_worked_golden(case):
+    if case["kind"] == "rotary":
+        got = oracle.rotary.rotate(np.array(_num(case["x"])), case["positions"],
+                                   np.array(_num(case["cos"])), np.array(_num(case["sin"])))
+        np.testing.assert_allclose(got, np.array(case["expected"], dtype=np.float64), rtol=0, atol=0)
+        return
     a = case["attrs"]
     kw = dict(scale=a["scale"], causal=a["causal"], window=a["window"],
               softcap=a["softcap"], smooth_softmax=a["smooth_softmax"],

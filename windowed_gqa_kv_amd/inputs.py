@@ -138,6 +138,17 @@ def generate(w: Workload, seed: Optional[int] = None) -> dict:
     return out
 
 
+def rotary_tables(max_pos: int, D: int, base: float = 10000.0):
+    """cos and sin tables [max_pos, D/2] (float32 CPU tensors) of the usual
+    rotary frequencies: row p, column i holds the angle p * base^(-2i/D).
+    These are inputs a caller supplies (a model's position tables), not part
+    of the attention arithmetic."""
+    i = np.arange(D // 2, dtype=np.float64)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * base ** (-2.0 * i / D)[None, :]
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)),
+            torch.from_numpy(np.sin(ang).astype(np.float32)))
+
+
 def to_f64(t):
     """Exact upcast of a (CPU or device) tensor to a float64 NumPy array."""
     if t is None:
