@@ -20,7 +20,9 @@ decode launches (one per cache replica); events around each eager launch,
 which also count its dispatch latency, are reported beside it.  `cpu_baseline` times the float64 oracle on
 this host (the oracle as it stands, on a bounded number of full decode
 steps).  `extra` reports the prompt workloads (TFLOP/s against the bf16 MFMA
-peak) and the speculative-decode workload the same way.
+peak) and the speculative-decode workload the same way; `rotary` times the
+rotary embedding of the long prompt's Q and K (GB/s against HBM) and a decode
+step's append with rotary beside the plain append.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
        [--no-cpu-baseline] [--workload NAME]
@@ -217,6 +219,84 @@ def bench_prefill(w, steps, warmup):
     return dict(ms_per_step=(t1 - t0) * 1000.0 / steps, flops=flops, kernel_ms=kms)
 
 
+def bench_rotary(steps, warmup):
+    """Rotary embedding: the long prompt's Q and K turned by gqa_apply_rotary
+    (HIP events around each launch; the inputs rotate over 8 replicas, 640 MiB,
+    so that no launch reads them from the Infinity Cache), and one decode
+    step's gqa_append_kv_rotary
+    against the plain gqa_append_kv (graphs of `steps` back-to-back launches,
+    HIP events around the replays)."""
+    import torch
+    from windowed_gqa_kv_amd import binding, work
+    from windowed_gqa_kv_amd.inputs import WORKLOADS, generate, rotary_tables
+
+    res = {}
+    wp = WORKLOADS[3]
+    d = generate(wp)
+    plan = binding.Plan(wp.Hq, wp.Hkv, wp.D, dtype=wp.dtype, local_window_size=wp.window,
+                        max_batch=wp.B, max_q_len=wp.Lq, max_kv_len=wp.Lk)
+    cos, sin = (t.cuda() for t in rotary_tables(wp.Lk, wp.D))
+    R = 8
+    q0, k0 = d["q"].cuda(), d["k"].cuda()
+    qs, ks = [q0.clone() for _ in range(R)], [k0.clone() for _ in range(R)]
+    qo, ko = torch.empty_like(q0), torch.empty_like(k0)
+    del d, q0, k0
+    for i in range(warmup):
+        plan.apply_rotary(qs[i % R], wp.Lk - wp.Lq, cos, sin, qo)
+        plan.apply_rotary(ks[i % R], 0, cos, sin, ko)
+    evq, evk = _events(steps), _events(steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evq[i][0].record()
+        plan.apply_rotary(qs[i % R], wp.Lk - wp.Lq, cos, sin, qo)
+        evq[i][1].record()
+        evk[i][0].record()
+        plan.apply_rotary(ks[(i + R // 2) % R], 0, cos, sin, ko)
+        evk[i][1].record()
+    torch.cuda.synchronize()
+    ms_q = sum(a.elapsed_time(b) for a, b in evq) / steps
+    ms_k = sum(a.elapsed_time(b) for a, b in evk) / steps
+    bq = work.rotary_bytes(wp.B * wp.Hq * wp.Lq, wp.D, wp.dtype, wp.Lq)
+    bk = work.rotary_bytes(wp.B * wp.Hkv * wp.Lk, wp.D, wp.dtype, wp.Lk)
+    res["prompt"] = {"workload": wp.name, "q_ms": round(ms_q, 5), "k_ms": round(ms_k, 5),
+                     "bytes": bq + bk, "achieved": round((bq + bk) / ((ms_q + ms_k) / 1e3) / 1e9, 2),
+                     "unit": "GB/s"}
+    res["prompt"]["frac"] = round(res["prompt"]["achieved"] / PEAK_HBM_GBS, 4)
+    del qs, ks, qo, ko
+    torch.cuda.empty_cache()
+
+    wd = WORKLOADS[2]
+    d = generate(wd)
+    plan = binding.Plan(wd.Hq, wd.Hkv, wd.D, dtype=wd.dtype, smooth_softmax=wd.smooth_softmax,
+                        max_batch=wd.B, max_q_len=wd.Lq, max_kv_len=wd.Lk)
+    cos, sin = (t.cuda() for t in rotary_tables(wd.Lk, wd.D))
+    kc, vc = d["k_cache"].cuda(), d["v_cache"].cuda()
+    q, kn, vn, seq = d["q"].cuda(), d["k_new"].cuda(), d["v_new"].cuda(), d["seqlens_k"].cuda()
+    q_rot = torch.empty_like(q)
+    calls = {"append_kv": lambda: plan.append_kv(kn, vn, kc, vc, seq),
+             "append_kv_rotary": lambda: plan.append_kv_rotary(q, kn, vn, kc, vc, seq, cos, sin, q_rot)}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        ev = _events(5)
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(min(a.elapsed_time(b) for a, b in ev) * 1e3 / steps, 3)
+    res["decode_step_workload"] = wd.name
+    res["append_kv_rotary_bytes"] = work.append_rotary_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.D, wd.dtype)
+    return res
+
+
 def cpu_baseline(w, d, budget_s=12.0):
     """The float64 oracle on full decode steps of the same workload, repeated
     until ~budget_s of CPU time; reported in the same unit (GB/s)."""
@@ -329,6 +409,7 @@ def main():
                                        "kernel_ms": round(rp["kernel_ms"], 5), "flops_per_launch": rp["flops"]}})
             torch.cuda.empty_cache()
         line["extra"] = extra
+        line["rotary"] = bench_rotary(args.extra_steps, 3)
 
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, r["inputs"])
     print(json.dumps(line), flush=True)

@@ -163,6 +163,52 @@ gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity
                       const int32_t* seqlens_k, const float* head_sink,
                       void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Rotary position tables supplied by the caller ("onnx: import
+ * GroupQueryAttention decode steps and its internal rotary", section "What
+ * changed": cos/sin caches with half the head size).  Device fp32, row-major
+ * [max_pos, head_size / 2], 16-byte aligned; row p holds the cosines
+ * (sines) of position p's angles, column i the angle of the pair
+ * (i, i + head_size/2).  Owned by the caller. */
+typedef struct {
+  const float* cos;
+  const float* sin;
+  int64_t max_pos;
+} gqa_rotary_tables;
+
+/* Rotary position embedding of rows [B, H, L, head_size] (do_rotary of the
+ * page above): element i pairs with i + head_size/2 and the pair turns by the
+ * angle of its row's position, (a, b) -> (a c - b s, b c + a s), computed in
+ * fp32 and rounded to the plan's dtype (nearest even).  Row l sits at
+ * position pos0 + l: a prompt on an empty past passes pos0 = Lk - Lq for Q
+ * and 0 for K (positions 0 .. S-1 when Lq = Lk = S), then calls gqa_prefill
+ * on the results.
+ *   x, y: [B, H, L, head_size] of the plan's dtype; y may be x itself (in
+ *     place) but must not otherwise overlap it.
+ * B, H or L == 0 is a no-op.
+ * Errors: INVALID_ARG (NULL or negative arguments), CAPACITY (pos0 + L >
+ *   tables->max_pos), UNSUPPORTED (alignment, sizes above 65535 / 2^30), HIP. */
+gqa_status gqa_apply_rotary(gqa_plan_t plan, int32_t B, int32_t H, int32_t L, int64_t pos0,
+                            gqa_tensor x, gqa_tensor y, const gqa_rotary_tables* tables,
+                            void* hip_stream);
+
+/* gqa_append_kv with rotary, in one launch: the curr new K rows are turned at
+ * their positions before they enter the cache (K is cached rotated, the page
+ * above), the new V rows are copied, and the curr query rows are turned into
+ * q_rot for the gqa_decode call that follows.  New token t of batch b sits at
+ * position total_b - curr + t, total_b = seqlens_k[b] + 1, which is also its
+ * cache slot (a single generated token: position seqlens_k[b]).
+ *   q, q_rot [B, Hq, curr, D] (q_rot may be q itself); k_new, v_new, k_cache,
+ *   v_cache and seqlens_k as in gqa_append_kv; tables as above.
+ * A batch with total_b < curr or total_b > capacity is skipped (its cache
+ * slots and q_rot rows are left as they are).
+ * Errors: as gqa_append_kv, and CAPACITY when tables->max_pos < capacity. */
+gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                gqa_tensor q, gqa_tensor q_rot,
+                                gqa_tensor k_new, gqa_tensor v_new,
+                                gqa_tensor k_cache, gqa_tensor v_cache,
+                                const int32_t* seqlens_k, const gqa_rotary_tables* tables,
+                                void* hip_stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* gqa_last_error(void);
 

@@ -154,6 +154,31 @@ def test_decode_validation():
     assert dec(curr=0) == B.GQA_OK
 
 
+def test_rotary_validation():
+    h = plan()
+    tab = B.gqa_rotary_tables(FAKE, FAKE, 64)
+    s = ctypes.c_void_p(FAKE)
+    def app(Bn=2, curr=1, cap=64, seq=s, tables=tab, **kw):
+        return B.gqa_append_kv_rotary(h, Bn, curr, cap, kw.get("q", t()), kw.get("qr", t()),
+                                      t(), t(), t(), t(), seq, tables, None)
+    def rot(Bn=2, H=8, L=8, pos0=0, tables=tab, **kw):
+        return B.gqa_apply_rotary(h, Bn, H, L, pos0, kw.get("x", t()), kw.get("y", t()), tables, None)
+    assert app(tables=None) == B.GQA_ERR_INVALID_ARG and "tables" in B.gqa_last_error()
+    assert app(tables=B.gqa_rotary_tables(0, FAKE, 64)) == B.GQA_ERR_INVALID_ARG
+    assert app(tables=B.gqa_rotary_tables(FAKE + 4, FAKE, 64)) == B.GQA_ERR_UNSUPPORTED
+    # every cache slot is a position: the tables must cover the capacity
+    assert app(cap=65) == B.GQA_ERR_CAPACITY and "rotary tables" in B.gqa_last_error()
+    assert app(curr=17) == B.GQA_ERR_CAPACITY
+    assert app(seq=None) == B.GQA_ERR_INVALID_ARG and "seqlens_k" in B.gqa_last_error()
+    assert app(qr=t(ptr=0)) == B.GQA_ERR_INVALID_ARG and "q_rot" in B.gqa_last_error()
+    assert app(Bn=0) == B.GQA_OK
+    assert rot(L=60, pos0=5) == B.GQA_ERR_CAPACITY and "rotary tables" in B.gqa_last_error()
+    assert rot(pos0=-1) == B.GQA_ERR_INVALID_ARG
+    assert rot(x=t(ptr=FAKE + 2)) == B.GQA_ERR_UNSUPPORTED and "aligned" in B.gqa_last_error()
+    assert rot(tables=B.gqa_rotary_tables(FAKE, FAKE, 0)) == B.GQA_ERR_INVALID_ARG
+    assert rot(L=0) == B.GQA_OK and rot(H=0) == B.GQA_OK
+
+
 def test_last_error_is_thread_local_and_specific():
     import threading
     B.gqa_plan(attrs(num_heads=0), 1, 1, 1)

@@ -31,7 +31,8 @@ GQA_F32, GQA_F16, GQA_BF16 = 0, 1, 2
 DTYPE_CODES = {"f32": GQA_F32, "f16": GQA_F16, "bf16": GQA_BF16}
 
 EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
-            "gqa_append_kv", "gqa_decode", "gqa_last_error")
+            "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
+            "gqa_last_error")
 
 
 class gqa_attrs(ctypes.Structure):
@@ -55,6 +56,14 @@ class gqa_tensor(ctypes.Structure):
         ("stride_b", ctypes.c_int64),
         ("stride_h", ctypes.c_int64),
         ("stride_s", ctypes.c_int64),
+    ]
+
+
+class gqa_rotary_tables(ctypes.Structure):
+    _fields_ = [
+        ("cos", ctypes.c_void_p),
+        ("sin", ctypes.c_void_p),
+        ("max_pos", ctypes.c_int64),
     ]
 
 
@@ -84,6 +93,11 @@ def load():
     lib.gqa_append_kv.restype = ctypes.c_int
     lib.gqa_decode.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P, S, P]
     lib.gqa_decode.restype = ctypes.c_int
+    RT = ctypes.POINTER(gqa_rotary_tables)
+    lib.gqa_apply_rotary.argtypes = [gqa_plan_t, I32, I32, I32, I64, T, T, RT, P]
+    lib.gqa_apply_rotary.restype = ctypes.c_int
+    lib.gqa_append_kv_rotary.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, T, T, P, RT, P]
+    lib.gqa_append_kv_rotary.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -123,6 +137,18 @@ def gqa_decode(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, hea
                ws_bytes, stream) -> int:
     return load().gqa_decode(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
                              head_sink, workspace, ws_bytes, stream)
+
+
+def gqa_apply_rotary(plan, B, H, L, pos0, x, y, tables, stream) -> int:
+    return load().gqa_apply_rotary(plan, B, H, L, pos0, x, y,
+                                   None if tables is None else ctypes.byref(tables), stream)
+
+
+def gqa_append_kv_rotary(plan, B, curr, capacity, q, q_rot, k_new, v_new, k_cache, v_cache,
+                         seqlens_k, tables, stream) -> int:
+    return load().gqa_append_kv_rotary(plan, B, curr, capacity, q, q_rot, k_new, v_new, k_cache,
+                                       v_cache, seqlens_k,
+                                       None if tables is None else ctypes.byref(tables), stream)
 
 
 def gqa_last_error() -> str:
@@ -262,3 +288,42 @@ class Plan:
                          _ptr(workspace), workspace.numel() * workspace.element_size(),
                          _stream(stream)))
         return out
+
+    @staticmethod
+    def _tables(cos, sin):
+        import torch
+        for t_ in (cos, sin):
+            if t_.dtype != torch.float32 or t_.dim() != 2 or not t_.is_contiguous():
+                raise ValueError("rotary tables must be contiguous float32 [max_pos, D/2]")
+        if cos.shape != sin.shape:
+            raise ValueError("cos and sin tables differ in shape")
+        return gqa_rotary_tables(cos.data_ptr(), sin.data_ptr(), cos.shape[0])
+
+    def apply_rotary(self, x, pos0, cos, sin, out=None, *, stream=None):
+        """Rotary embedding of x [B, H, L, D] at positions pos0 + l (out may be x)."""
+        import torch
+        self._check_dtype(x)
+        if cos.shape[1] * 2 != self.head_size:
+            raise ValueError("rotary tables need head_size / 2 columns")
+        if out is None:
+            out = torch.empty_like(x)
+        B, H, L, _ = x.shape
+        check(gqa_apply_rotary(self._h, B, H, L, pos0, tensor_view(x), tensor_view(out),
+                               self._tables(cos, sin), _stream(stream)))
+        return out
+
+    def append_kv_rotary(self, q, k_new, v_new, k_cache, v_cache, seqlens_k, cos, sin,
+                         q_rot=None, *, stream=None):
+        """One decode step's append with rotary; returns the rotated q (q_rot may be q)."""
+        import torch
+        self._check_dtype(q, k_new, v_new, k_cache, v_cache)
+        if cos.shape[1] * 2 != self.head_size:
+            raise ValueError("rotary tables need head_size / 2 columns")
+        if q_rot is None:
+            q_rot = torch.empty_like(q)
+        B, _, curr, _ = k_new.shape
+        check(gqa_append_kv_rotary(self._h, B, curr, k_cache.shape[2], tensor_view(q),
+                                   tensor_view(q_rot), tensor_view(k_new), tensor_view(v_new),
+                                   tensor_view(k_cache), tensor_view(v_cache), _ptr(seqlens_k),
+                                   self._tables(cos, sin), _stream(stream)))
+        return q_rot

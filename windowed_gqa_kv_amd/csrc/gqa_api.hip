@@ -282,4 +282,102 @@ GQA_API gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t 
   return hip_status(gqa::launch_attn_generic(a, dtype, stream), "decode launch");
 }
 
+namespace {
+
+gqa_status check_tables(const gqa_rotary_tables* t, int64_t need_pos) {
+  if (t == nullptr) return fail(GQA_ERR_INVALID_ARG, "rotary tables are NULL");
+  if (t->cos == nullptr || t->sin == nullptr) return fail(GQA_ERR_INVALID_ARG, "rotary cos/sin table is NULL");
+  if (reinterpret_cast<uintptr_t>(t->cos) % 16 != 0 || reinterpret_cast<uintptr_t>(t->sin) % 16 != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "rotary tables must be 16-byte aligned");
+  if (t->max_pos < 1) return fail(GQA_ERR_INVALID_ARG, "rotary max_pos must be >= 1");
+  if (need_pos > t->max_pos)
+    return fail(GQA_ERR_CAPACITY, "positions up to %lld need rotary tables of at least %lld rows (got %lld)",
+                (long long)need_pos - 1, (long long)need_pos, (long long)t->max_pos);
+  return GQA_OK;
+}
+
+void set_job(gqa::RotaryArgs& a, int j, const gqa_tensor& src, const gqa_tensor& dst, int H, int turn,
+             int to_slot) {
+  a.src[j] = src.data;
+  a.dst[j] = dst.data;
+  a.s_sb[j] = src.stride_b; a.s_sh[j] = src.stride_h; a.s_ss[j] = src.stride_s;
+  a.d_sb[j] = dst.stride_b; a.d_sh[j] = dst.stride_h; a.d_ss[j] = dst.stride_s;
+  a.H[j] = H;
+  a.turn[j] = turn;
+  a.to_slot[j] = to_slot;
+}
+
+}  // namespace
+
+GQA_API gqa_status gqa_apply_rotary(gqa_plan_t plan, int32_t B, int32_t H, int32_t L, int64_t pos0,
+                                    gqa_tensor x, gqa_tensor y, const gqa_rotary_tables* tables,
+                                    void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || H < 0 || L < 0 || pos0 < 0) return fail(GQA_ERR_INVALID_ARG, "B, H, L and pos0 must be >= 0");
+  if (B > 65535 || H > 65535) return fail(GQA_ERR_UNSUPPORTED, "B and H must be <= 65535");
+  if (L > kMaxLen || pos0 > kMaxLen) return fail(GQA_ERR_UNSUPPORTED, "positions above 2^30");
+  gqa_status st = check_tables(tables, pos0 + L);
+  if (st != GQA_OK) return st;
+  if (B == 0 || H == 0 || L == 0) return GQA_OK;
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("x", x, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("y", y, esz)) != GQA_OK) return st;
+  gqa::RotaryArgs a{};
+  set_job(a, 0, x, y, H, 1, 0);
+  a.jobs = 1;
+  a.B = B;
+  a.L = L;
+  a.D = plan->attrs.head_size;
+  a.pos0 = pos0;
+  a.seqlens = nullptr;
+  a.cos = tables->cos;
+  a.sin = tables->sin;
+  a.max_pos = tables->max_pos;
+  return hip_status(gqa::launch_rotary(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
+                    "rotary launch");
+}
+
+GQA_API gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                        gqa_tensor q, gqa_tensor q_rot, gqa_tensor k_new, gqa_tensor v_new,
+                                        gqa_tensor k_cache, gqa_tensor v_cache, const int32_t* seqlens_k,
+                                        const gqa_rotary_tables* tables, void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (curr > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the plan's max_q_len %d", curr, plan->max_q_len);
+  if (capacity > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
+                (long long)plan->max_kv_len);
+  if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  // every position is a cache slot below capacity
+  gqa_status st = check_tables(tables, capacity);
+  if (st != GQA_OK) return st;
+  if (B == 0 || curr == 0) return GQA_OK;
+  if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("q", q, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("q_rot", q_rot, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_new", k_new, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("v_new", v_new, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, esz)) != GQA_OK) return st;
+  gqa::RotaryArgs a{};
+  set_job(a, 0, k_new, k_cache, plan->attrs.kv_num_heads, 1, 1);
+  set_job(a, 1, v_new, v_cache, plan->attrs.kv_num_heads, 0, 1);
+  set_job(a, 2, q, q_rot, plan->attrs.num_heads, 1, 0);
+  a.jobs = 3;
+  a.B = B;
+  a.L = curr;
+  a.D = plan->attrs.head_size;
+  a.pos0 = 0;
+  a.seqlens = seqlens_k;
+  a.capacity = (int32_t)capacity;
+  a.cos = tables->cos;
+  a.sin = tables->sin;
+  a.max_pos = tables->max_pos;
+  return hip_status(gqa::launch_rotary(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
+                    "append_kv_rotary launch");
+}
+
 GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }

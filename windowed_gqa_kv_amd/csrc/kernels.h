@@ -56,4 +56,30 @@ struct AppendArgs {
 };
 hipError_t launch_append_kv(const AppendArgs& a, hipStream_t stream);
 
+// Rotary position embedding: up to three jobs in one launch (blockIdx.y),
+// each turning (turn = 1) or copying (turn = 0) rows [B, H[j], L, D] of
+// src[j] into dst[j].  Row l of batch b sits at position pos0 + l, or, when
+// seqlens is set (a decode step of L = curr tokens), at seqlens[b] + 1 - L + l,
+// batches whose length falls outside [L, capacity] being skipped; to_slot[j]
+// writes it to the row of its position instead of row l.  Strides are in
+// elements; tables are fp32 [max_pos, D/2].
+struct RotaryArgs {
+  const void* src[3];
+  void* dst[3];
+  int64_t s_sb[3], s_sh[3], s_ss[3];
+  int64_t d_sb[3], d_sh[3], d_ss[3];
+  int32_t H[3];
+  int32_t turn[3];
+  int32_t to_slot[3];
+  int32_t jobs;
+  int32_t B, L, D;
+  int64_t pos0;
+  const int32_t* seqlens;
+  int32_t capacity;
+  const float* cos;
+  const float* sin;
+  int64_t max_pos;
+};
+hipError_t launch_rotary(const RotaryArgs& a, int dtype, hipStream_t stream);
+
 }  // namespace gqa

@@ -84,3 +84,19 @@ def decode_flops(seqlens_k, curr, Hq, D, causal, window) -> int:
 def append_bytes(B, Hkv, curr, D, dtype) -> int:
     """K and V rows read from the step buffers and written into the cache."""
     return 2 * 2 * B * Hkv * curr * D * ELEM_BYTES[dtype]
+
+
+def rotary_bytes(rows: int, D: int, dtype: str, positions: int) -> int:
+    """Rotary embedding of `rows` rows of D elements at `positions` distinct
+    positions: every row read and written once, and the cos and sin table
+    rows (D/2 fp32 each) of those positions read once."""
+    return 2 * rows * D * ELEM_BYTES[dtype] + positions * D * 4
+
+
+def append_rotary_bytes(B, Hq, Hkv, curr, D, dtype) -> int:
+    """One decode step's append with rotary: the new K and V rows read and
+    written into the cache, the query rows read and written turned, and the
+    table rows of the B * curr positions read."""
+    e = ELEM_BYTES[dtype]
+    return 2 * (2 * B * Hkv + B * Hq) * curr * D * e + B * curr * D * 4
+
