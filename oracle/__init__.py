@@ -9,6 +9,7 @@ nothing from the product path.
 ``attention``  plain materialized float64 attention (NumPy), the definition.
 ``brute``      the same definition with scalar Python loops, for tiny shapes.
 ``rotary``     rotary position embedding of Q and of K before it enters the cache.
+``rolling``    the rolling (ring-buffer) KV cache of a windowed layer.
 """
 
 from .materialized import (  # noqa: F401
@@ -22,3 +23,4 @@ from .materialized import (  # noqa: F401
 )
 from . import brute  # noqa: F401
 from . import rotary  # noqa: F401
+from . import rolling  # noqa: F401
