@@ -64,17 +64,18 @@ def append(k_ring, v_ring, k_new, v_new, seqlens_k):
     return kr, vr
 
 
-def linear_history(ring, seqlens_k):
-    """[B, H, max_total, D] with the key of position j at index j for the
-    positions the ring still holds (j >= total_b - C); older positions, whose
-    slots were overwritten, are NaN (they must never be read)."""
+def linear_history(ring, seqlens_k, start: int = 0):
+    """[B, H, max_total - start, D] with the key of position j at index
+    j - start for the positions the ring still holds (j >= total_b - C);
+    older positions, whose slots were overwritten, are NaN (they must never
+    be read)."""
     ring = np.asarray(ring, dtype=np.float64)
     B, H, C, D = ring.shape
     total = _totals(seqlens_k, B)
-    out = np.full((B, H, int(total.max()), D), np.nan)
+    out = np.full((B, H, int(total.max()) - start, D), np.nan)
     for b in range(B):
-        for j in range(max(0, int(total[b]) - C), int(total[b])):
-            out[b, :, j] = ring[b, :, int(slot_of(j, C))]
+        for j in range(max(start, int(total[b]) - C), int(total[b])):
+            out[b, :, j - start] = ring[b, :, int(slot_of(j, C))]
     return out
 
 
@@ -88,7 +89,14 @@ def decode(q, k_ring, v_ring, seqlens_k, *, scale: float, window: int, causal: b
         raise ValueError("a rolling cache needs the window on")
     if C < window + curr - 1:
         raise ValueError("ring too small: need capacity >= window + curr - 1")
-    kl = linear_history(k_ring, seqlens_k)
-    vl = linear_history(v_ring, seqlens_k)
-    return _decode(q, kl, vl, seqlens_k, scale=scale, causal=causal, window=window,
+    # Only positions from `start` on can be seen by any batch (each batch's
+    # rows reach back at most C positions).  The allowed set depends on
+    # position differences and on j < total only, so moving every position
+    # down by `start` changes nothing; it keeps the materialized history small
+    # when positions are large.
+    total = _totals(seqlens_k, q.shape[0])
+    start = int(max(0, total.min() - C))
+    kl = linear_history(k_ring, seqlens_k, start)
+    vl = linear_history(v_ring, seqlens_k, start)
+    return _decode(q, kl, vl, total - 1 - start, scale=scale, causal=causal, window=window,
                    softcap=softcap, smooth_softmax=smooth_softmax, head_sink=head_sink)

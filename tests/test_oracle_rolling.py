@@ -86,6 +86,39 @@ def test_overwritten_positions_are_absent_from_the_history():
     assert np.isnan(hist[1, 0, 4:]).all()
 
 
+def test_batches_of_different_lengths():
+    """Per-batch histories of different lengths (some never wrapped); the
+    ring is filled by placing position p at slot p mod C directly."""
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, D, C, W, curr = 3, 4, 2, 8, 9, 7, 3
+    totals = np.array([40, 12, 5])
+    k_hist, v_hist = _history(rng, B, Hkv, int(totals.max()), D)
+    kr = rng.standard_normal((B, Hkv, C, D))
+    vr = rng.standard_normal((B, Hkv, C, D))
+    for b in range(B):
+        for p in range(max(0, totals[b] - C), totals[b]):
+            kr[b, :, p % C] = k_hist[b, :, p]
+            vr[b, :, p % C] = v_hist[b, :, p]
+    q = rng.standard_normal((B, Hq, curr, D))
+    got = roll.decode(q, kr, vr, totals - 1, scale=0.5, window=W, smooth_softmax=True)
+    want = oracle.decode(q, k_hist, v_hist, totals - 1, scale=0.5, window=W, smooth_softmax=True)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+
+
+def test_far_positions_give_the_same_result():
+    """Moving every position by a multiple of the ring (same slots) leaves
+    the decode unchanged: only position differences matter."""
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, D, C, W, curr = 2, 4, 2, 8, 9, 6, 4
+    ring_k, ring_v = rng.standard_normal((B, Hkv, C, D)), rng.standard_normal((B, Hkv, C, D))
+    q = rng.standard_normal((B, Hq, curr, D))
+    near = np.array([20, 13])
+    far = near + 1000 * C
+    a = roll.decode(q, ring_k, ring_v, near, scale=0.3, window=W)
+    b = roll.decode(q, ring_k, ring_v, far, scale=0.3, window=W)
+    np.testing.assert_array_equal(a, b)
+
+
 def test_rolling_rejects_a_ring_that_loses_needed_keys():
     z = np.zeros((1, 2, 1, 4))
     ring = np.zeros((1, 1, 6, 4))
@@ -111,7 +144,9 @@ def _mutant(old, new):
 @pytest.mark.parametrize("old,new", [
     ("return np.asarray(p) % capacity", "return (np.asarray(p) + 1) % capacity"),          # slot shifted
     ("s = int(slot_of(total[b] - curr + t, C))", "s = int(slot_of(total[b] - curr + t - 1, C))"),  # append late
-    ("range(max(0, int(total[b]) - C), int(total[b]))", "range(max(0, int(total[b]) - C + 1), int(total[b]))"),  # oldest kept key dropped
+    ("range(max(start, int(total[b]) - C), int(total[b]))",
+     "range(max(start, int(total[b]) - C + 1), int(total[b]))"),                           # oldest kept key dropped
+    ("start = int(max(0, total.min() - C))", "start = int(max(0, total.max() - C))"),     # trims keys a batch needs
     ("if C < window + curr - 1:", "if C < window:"),                                        # capacity rule too weak
 ])
 def test_rolling_pins_catch_planted_mistakes(monkeypatch, old, new):
@@ -121,7 +156,9 @@ def test_rolling_pins_catch_planted_mistakes(monkeypatch, old, new):
     try:
         for args in [(7, 5, 3, [4, 3, 3, 1, 2, 5, 3]), (10, 4, 1, [9, 1, 1, 1, 1, 1, 1, 1])]:
             test_rolling_decode_equals_window_over_full_history(*args)
+        test_rolling_decode_equals_window_over_full_history(16, 6, 4, [3, 8, 4, 4, 4, 4, 4, 4, 4])
         test_append_writes_only_the_step_slots_across_the_wrap()
+        test_batches_of_different_lengths()
         test_overwritten_positions_are_absent_from_the_history()
         test_rolling_rejects_a_ring_that_loses_needed_keys()
     except (AssertionError, ValueError, pytest.fail.Exception):
