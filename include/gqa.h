@@ -83,6 +83,13 @@ typedef struct {
   int32_t use_head_sink;     /* 0/1: a per-query-head fp32 sink logit array is passed */
   int32_t is_causal;         /* 1 = bottom-right causal band; 0 only with W == -1 */
   gqa_dtype dtype;           /* element type of every tensor argument */
+  int32_t rolling_cache;     /* 0/1: the KV cache is a ring (sliding_window_cache, "[NPUW]
+                              * Support GQA sliding-window ...", section "Sliding window
+                              * (local_window_size)"): the token at position p lives in slot
+                              * p mod capacity, positions may pass the capacity, and every
+                              * call needs capacity >= W + curr - 1 (so every key a step may
+                              * see is still held).  Needs W >= 1.  Affects gqa_append_kv,
+                              * gqa_append_kv_rotary and gqa_decode only. */
 } gqa_attrs;
 
 /* A strided 4-D view [B][H][L][D] with a contiguous last dimension.  Strides
@@ -135,10 +142,12 @@ gqa_status gqa_prefill(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk,
 /* Append curr new K/V rows per (batch, KV head) to the cache: row t goes to
  * slot total_b - curr + t, total_b = seqlens_k[b] + 1 (present =
  * concat(past, step), "onnx: import GroupQueryAttention decode steps ...",
- * section "What changed").
+ * section "What changed"); with attrs.rolling_cache, to slot
+ * (total_b - curr + t) mod capacity.
  *   k_new, v_new [B, Hkv, curr, D]   k_cache, v_cache [B, Hkv, capacity, D]
  *   seqlens_k: device int32 [B] (a [B,1] array is the same memory).
- * A batch with total_b < curr or total_b > capacity is skipped.
+ * A batch with total_b < curr, or (without rolling_cache) total_b > capacity,
+ * is skipped.
  * Errors: INVALID_ARG, CAPACITY (curr > capacity or above plan maxima),
  *   UNSUPPORTED, HIP. */
 gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
@@ -151,6 +160,10 @@ gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capac
  * at position total_b - curr + t; keys are the slots [0, total_b) ("[NPUW]
  * Support GQA sliding-window ...", section "Sliding window
  * (local_window_size)"; causal inside the step: row t sees new tokens <= t).
+ * With attrs.rolling_cache the key at position j is read from slot
+ * j mod capacity; the result is the windowed attention over the whole
+ * history (the same page: the window as a mask over the full cache and the
+ * rolling buffer give the same result), which needs capacity >= W + curr - 1.
  *   q, out [B, Hq, curr, D]   k_cache, v_cache [B, Hkv, capacity, D]
  *   seqlens_k: device int32 [B]; head_sink as in gqa_prefill.
  *   workspace: device, >= gqa_workspace_size(plan) bytes, 16-byte aligned,
@@ -196,10 +209,14 @@ gqa_status gqa_apply_rotary(gqa_plan_t plan, int32_t B, int32_t H, int32_t L, in
  * above), the new V rows are copied, and the curr query rows are turned into
  * q_rot for the gqa_decode call that follows.  New token t of batch b sits at
  * position total_b - curr + t, total_b = seqlens_k[b] + 1, which is also its
- * cache slot (a single generated token: position seqlens_k[b]).
+ * cache slot (a single generated token: position seqlens_k[b]); with
+ * attrs.rolling_cache the slot is that position mod capacity, positions may
+ * pass the capacity, and rows whose position is at or past tables->max_pos
+ * are left unwritten (the host cannot see the lengths).
  *   q, q_rot [B, Hq, curr, D] (q_rot may be q itself); k_new, v_new, k_cache,
  *   v_cache and seqlens_k as in gqa_append_kv; tables as above.
- * A batch with total_b < curr or total_b > capacity is skipped (its cache
+ * A batch with total_b < curr, or (without rolling_cache) total_b > capacity,
+ * is skipped (its cache
  * slots and q_rot rows are left as they are).
  * Errors: as gqa_append_kv, and CAPACITY when tables->max_pos < capacity. */
 gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,

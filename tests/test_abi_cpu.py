@@ -179,6 +179,31 @@ def test_rotary_validation():
     assert rot(L=0) == B.GQA_OK and rot(H=0) == B.GQA_OK
 
 
+def test_rolling_cache_validation():
+    st, _ = B.gqa_plan(attrs(rolling_cache=1), 4, 16, 1024)  # window off
+    assert st == B.GQA_ERR_INVALID_ARG and "rolling_cache" in B.gqa_last_error()
+    st, _ = B.gqa_plan(attrs(rolling_cache=2, local_window_size=8), 4, 16, 1024)
+    assert st == B.GQA_ERR_INVALID_ARG
+    h = plan(rolling_cache=1, local_window_size=100)
+    s = ctypes.c_void_p(FAKE)
+    ws = B.gqa_workspace_size(h)
+    # the ring must hold W + curr - 1 keys: 100 + 4 - 1 = 103
+    assert B.gqa_append_kv(h, 2, 4, 102, t(), t(), t(), t(), s, None) == B.GQA_ERR_CAPACITY
+    assert "rolling" in B.gqa_last_error()
+    assert B.gqa_decode(h, 2, 4, 102, t(), t(), t(), t(), s, None, ctypes.c_void_p(FAKE), ws,
+                        None) == B.GQA_ERR_CAPACITY
+    tab = B.gqa_rotary_tables(FAKE, FAKE, 64)
+    assert B.gqa_append_kv_rotary(h, 2, 4, 102, t(), t(), t(), t(), t(), t(), s, tab,
+                                  None) == B.GQA_ERR_CAPACITY
+    # exactly enough passes validation (B = 0: nothing is launched)
+    assert B.gqa_append_kv(h, 0, 4, 103, t(), t(), t(), t(), s, None) == B.GQA_OK
+    assert B.gqa_decode(h, 0, 4, 103, t(), t(), t(), t(), s, None, ctypes.c_void_p(FAKE), ws,
+                        None) == B.GQA_OK
+    # a rolling cache's positions pass the capacity: the tables need not cover it
+    assert B.gqa_append_kv_rotary(h, 0, 4, 103, t(), t(), t(), t(), t(), t(), s, tab,
+                                  None) == B.GQA_OK
+
+
 def test_last_error_is_thread_local_and_specific():
     import threading
     B.gqa_plan(attrs(num_heads=0), 1, 1, 1)

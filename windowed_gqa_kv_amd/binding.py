@@ -47,6 +47,7 @@ class gqa_attrs(ctypes.Structure):
         ("use_head_sink", ctypes.c_int32),
         ("is_causal", ctypes.c_int32),
         ("dtype", ctypes.c_int),
+        ("rolling_cache", ctypes.c_int32),
     ]
 
 
@@ -212,11 +213,11 @@ class Plan:
     def __init__(self, num_heads: int, kv_num_heads: int, head_size: int, *, dtype: str,
                  scale: float = 0.0, local_window_size: int = -1, softcap: float = 0.0,
                  smooth_softmax: bool = False, use_head_sink: bool = False,
-                 is_causal: bool = True, max_batch: int = 1, max_q_len: int = 1,
-                 max_kv_len: int = 1):
+                 is_causal: bool = True, rolling_cache: bool = False, max_batch: int = 1,
+                 max_q_len: int = 1, max_kv_len: int = 1):
         self.attrs = gqa_attrs(num_heads, kv_num_heads, head_size, scale, local_window_size,
                                softcap, int(smooth_softmax), int(use_head_sink), int(is_causal),
-                               DTYPE_CODES[dtype])
+                               DTYPE_CODES[dtype], int(rolling_cache))
         self.dtype = dtype
         self.num_heads, self.kv_num_heads, self.head_size = num_heads, kv_num_heads, head_size
         self._h = None

@@ -5,7 +5,9 @@
 // import GroupQueryAttention decode steps and its internal rotary", section
 // "What changed"; decode positions (total - curr) + i, "[NPUW] Support GQA
 // sliding-window and smooth-softmax in DecomposeGQA", section "Sliding window
-// (local_window_size)").  One thread moves 16 bytes; blockIdx.y selects K or V.
+// (local_window_size)"); a rolling cache (the same page: sliding_window_cache)
+// keeps position p in slot p mod capacity.  One thread moves 16 bytes;
+// blockIdx.y selects K or V.
 #include "kernels.h"
 
 namespace gqa {
@@ -33,8 +35,9 @@ __global__ __launch_bounds__(256) void append_kv_kernel(AppendArgs a) {
   const u32x4 x = *reinterpret_cast<const u32x4*>(src + so + 16 * c);
   const int64_t total = (int64_t)a.seqlens[b] + 1;
   asm volatile("" ::"v"(x));
-  if (total < a.curr || total > a.capacity) return;  // out-of-range length: skip batch
-  const int64_t slot = total - a.curr + t;
+  if (total < a.curr || (!a.rolling && total > a.capacity)) return;  // out-of-range length: skip batch
+  int64_t slot = total - a.curr + t;
+  if (a.rolling) slot %= a.capacity;  // a rolling cache: the position's ring slot
   char* dst = reinterpret_cast<char*>(is_v ? a.v_cache : a.k_cache);
   const int64_t dof = is_v ? (b * a.vc_sb + g * a.vc_sh + slot * a.vc_ss)
                            : (b * a.kc_sb + g * a.kc_sh + slot * a.kc_ss);

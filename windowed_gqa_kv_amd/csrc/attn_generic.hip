@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
       float dot = 0.0f;
       for (int d0 = 0; d0 < a.D; d0 += 8) {
         float kx[8], qx[8];
-        load8<DT>(a.k, k_base + (int64_t)j * a.k_ss + d0, kx);
+        load8<DT>(a.k, k_base + (int64_t)slot_of(a, j) * a.k_ss + d0, kx);
         load8<DT>(a.q, q_off + d0, qx);
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot = fmaf(qx[e], kx[e], dot);
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
     const int nk = min(64, hi - kb + 1);
     for (int jj = 0; jj < nk; ++jj) {
       const float pv = __shfl(pj, jj, 64);
-      const int64_t vrow = v_base + (int64_t)(kb + jj) * a.v_ss;
+      const int64_t vrow = v_base + (int64_t)slot_of(a, kb + jj) * a.v_ss;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int d = lane + 64 * c;

@@ -22,6 +22,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int32_t kMaxPosition = 1 << 30;  // positions stay in 32-bit arithmetic
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
@@ -30,6 +31,8 @@ constexpr int kWave = 64;
 // mode 0 (prompt):  q_offset = Lk - Lq; valid = nonpad[b] (or Lk).
 // mode 1 (decode):  total = seqlens[b] + 1; q_offset = total - Lq; valid = total.
 // An out-of-range device length turns that batch's rows into zeros.
+// ring > 0 (decode on a rolling cache of `ring` = Lk slots): the key at
+// position j lives in slot j mod ring and total may pass the capacity.
 // ---------------------------------------------------------------------------
 struct AttnArgs {
   const void* q;
@@ -50,6 +53,7 @@ struct AttnArgs {
   int32_t causal;
   int32_t window;   // -1 = off
   int32_t use_sink;
+  int32_t ring;         // 0, or the slot count of a rolling cache (decode)
   float scale_log2;     // scale * log2(e)
   float scale_over_cap; // scale / softcap (softcap > 0 only)
   float cap_log2;       // softcap * log2(e)
@@ -69,7 +73,7 @@ __device__ __forceinline__ BatchSpan batch_span(const AttnArgs& a, int b) {
     s.q_off = a.Lk - a.Lq;
   } else {
     int64_t total = (int64_t)a.seqlens[b] + 1;
-    bool ok = total >= a.Lq && total <= a.Lk;
+    bool ok = total >= a.Lq && total <= (a.ring ? (int64_t)kMaxPosition : (int64_t)a.Lk);
     s.valid = ok ? (int)total : 0;
     s.q_off = ok ? (int)(total - a.Lq) : 0;
   }
@@ -83,6 +87,11 @@ __device__ __forceinline__ int row_lo(const AttnArgs& a, int p) {
 }
 __device__ __forceinline__ int row_hi(const AttnArgs& a, int p, int valid) {
   return a.causal ? min(p, valid - 1) : valid - 1;
+}
+
+// Cache slot of the key at position j (a rolling cache wraps it).
+__device__ __forceinline__ int slot_of(const AttnArgs& a, int j) {
+  return a.ring ? j % a.ring : j;
 }
 
 // Sink logit of query head h in log2 units.

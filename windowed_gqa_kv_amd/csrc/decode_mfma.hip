@@ -639,9 +639,15 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
 
     // units of this wave: ua + w, ua + w + 4, ...
     const int nw = ub - ua > w ? (ub - ua - w + 3) / 4 : 0;
+    // A rolling cache keeps position j in slot j mod ring.  The piece spans
+    // fewer than `ring` positions (the host checks capacity >= W + curr - 1),
+    // so after removing the whole turns before c_lo one conditional wrap maps
+    // every key.  Caches that are not rings take the plain addresses (a
+    // wave-uniform branch per unit).
+    const int turns = a.ring ? c_lo - c_lo % a.ring : 0;
     // Rows past the piece end are clamped to its last key (a real key,
     // finite, masked out for every query row): no per-lane branches.
-    auto issue = [&](int s, int j) {
+    auto issue_t = [&](int s, int j, auto ring_tag) {
       const int kb = c_lo + kSub * (w + 4 * j);
       unsigned char* kdst = my_ring + s * 2 * RG::kUnitBytes;
       unsigned char* vdst = kdst + RG::kUnitBytes;
@@ -650,13 +656,23 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
         const int pos = 64 * i + lane;                 // 16-byte chunk position in the unit
         const int key = pos / RG::kSlots;
         const int cc = (pos % RG::kSlots) ^ swz<D>(key);  // the global chunk stored there
-        const int row = min(kb + key, c_hi);
+        int row = min(kb + key, c_hi);
+        if constexpr (decltype(ring_tag)::value) {
+          row -= turns;
+          row = row >= a.ring ? row - a.ring : row;
+        }
         // K/V bytes are read once per call: non-temporal (streaming) loads
         __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)row * a.k_ss + 8 * cc),
                                          (lds_void*)(kdst + 1024 * i), 16, 0, kNonTemporal);
         __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)row * a.v_ss + 8 * cc),
                                          (lds_void*)(vdst + 1024 * i), 16, 0, kNonTemporal);
       }
+    };
+    auto issue = [&](int s, int j) {
+      if (a.ring)
+        issue_t(s, j, std::true_type{});
+      else
+        issue_t(s, j, std::false_type{});
     };
     const int npro = min(nw, S);
     for (int j = 0; j < npro; ++j) issue(j, j);

@@ -87,11 +87,22 @@ gqa::AttnArgs make_args(const gqa_plan_s* p, const gqa_tensor& q, const gqa_tens
   a.causal = p->attrs.is_causal;
   a.window = p->attrs.local_window_size;
   a.use_sink = (p->attrs.use_head_sink || p->attrs.smooth_softmax) ? 1 : 0;
+  a.ring = (mode == 1 && p->attrs.rolling_cache) ? (int32_t)Lk : 0;
   const float log2e = 1.4426950408889634f;
   a.scale_log2 = p->scale * log2e;
   a.scale_over_cap = p->attrs.softcap > 0 ? p->scale / p->attrs.softcap : 0.0f;
   a.cap_log2 = p->attrs.softcap > 0 ? p->attrs.softcap * log2e : 0.0f;
   return a;
+}
+
+// A rolling cache must still hold every key a step's rows may see.
+gqa_status check_ring(const gqa_plan_s* p, int32_t curr, int64_t capacity) {
+  if (!p->attrs.rolling_cache) return GQA_OK;
+  const int64_t need = (int64_t)p->attrs.local_window_size + curr - 1;
+  if (capacity < need)
+    return fail(GQA_ERR_CAPACITY, "a rolling cache of %lld slots loses keys the step needs: capacity >= "
+                "local_window_size + curr - 1 = %lld", (long long)capacity, (long long)need);
+  return GQA_OK;
 }
 
 gqa_status check_sink(const gqa_plan_s* p, const float* head_sink) {
@@ -133,6 +144,9 @@ GQA_API gqa_status gqa_plan(const gqa_attrs* attrs, int32_t max_batch, int32_t m
   if (a.use_head_sink != 0 && a.use_head_sink != 1)
     return fail(GQA_ERR_INVALID_ARG, "use_head_sink must be 0 or 1");
   if (a.is_causal != 0 && a.is_causal != 1) return fail(GQA_ERR_INVALID_ARG, "is_causal must be 0 or 1");
+  if (a.rolling_cache != 0 && a.rolling_cache != 1) return fail(GQA_ERR_INVALID_ARG, "rolling_cache must be 0 or 1");
+  if (a.rolling_cache && a.local_window_size < 1)
+    return fail(GQA_ERR_INVALID_ARG, "rolling_cache needs local_window_size >= 1 (the ring holds the window)");
   if (!a.is_causal && a.local_window_size != -1)
     return fail(GQA_ERR_INVALID_ARG, "local_window_size needs is_causal = 1 (the window is one-sided)");
   if (max_batch < 1 || max_q_len < 1 || max_kv_len < 1)
@@ -213,10 +227,11 @@ GQA_API gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64
     return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
                 (long long)plan->max_kv_len);
   if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  gqa_status st = check_ring(plan, curr, capacity);
+  if (st != GQA_OK) return st;
   if (B == 0 || curr == 0) return GQA_OK;
   if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
   const int esz = elem_size(plan->attrs.dtype);
-  gqa_status st;
   if ((st = check_tensor("k_new", k_new, esz)) != GQA_OK) return st;
   if ((st = check_tensor("v_new", v_new, esz)) != GQA_OK) return st;
   if ((st = check_tensor("k_cache", k_cache, esz)) != GQA_OK) return st;
@@ -236,6 +251,7 @@ GQA_API gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64
   a.curr = curr;
   a.row_bytes = plan->attrs.head_size * esz;
   a.capacity = (int32_t)capacity;
+  a.rolling = plan->attrs.rolling_cache;
   return hip_status(gqa::launch_append_kv(a, reinterpret_cast<hipStream_t>(hip_stream)), "append_kv launch");
 }
 
@@ -254,6 +270,7 @@ GQA_API gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t 
   if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
   gqa_status st = check_sink(plan, head_sink);
   if (st != GQA_OK) return st;
+  if ((st = check_ring(plan, curr, capacity)) != GQA_OK) return st;
   if (B == 0 || curr == 0) return GQA_OK;
   if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
   const int esz = elem_size(plan->attrs.dtype);
@@ -350,9 +367,11 @@ GQA_API gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr
     return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
                 (long long)plan->max_kv_len);
   if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
-  // every position is a cache slot below capacity
-  gqa_status st = check_tables(tables, capacity);
+  // every position is a cache slot below capacity (a rolling cache's positions
+  // pass it: rows at or past max_pos are left unwritten by the kernel)
+  gqa_status st = check_tables(tables, plan->attrs.rolling_cache ? 1 : capacity);
   if (st != GQA_OK) return st;
+  if ((st = check_ring(plan, curr, capacity)) != GQA_OK) return st;
   if (B == 0 || curr == 0) return GQA_OK;
   if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
   const int esz = elem_size(plan->attrs.dtype);
@@ -373,6 +392,7 @@ GQA_API gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr
   a.pos0 = 0;
   a.seqlens = seqlens_k;
   a.capacity = (int32_t)capacity;
+  a.rolling = plan->attrs.rolling_cache;
   a.cos = tables->cos;
   a.sin = tables->sin;
   a.max_pos = tables->max_pos;

@@ -53,6 +53,7 @@ struct AppendArgs {
   const int32_t* seqlens;
   int32_t B, Hkv, curr, row_bytes;
   int32_t capacity;
+  int32_t rolling;  // 1: slot = position mod capacity, positions may pass it
 };
 hipError_t launch_append_kv(const AppendArgs& a, hipStream_t stream);
 
@@ -76,6 +77,7 @@ struct RotaryArgs {
   int64_t pos0;
   const int32_t* seqlens;
   int32_t capacity;
+  int32_t rolling;            // step mode: slot = position mod capacity, positions may pass it
   const float* cos;
   const float* sin;
   int64_t max_pos;

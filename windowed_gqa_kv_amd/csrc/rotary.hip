@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void rotary_kernel(RotaryArgs a) {
   int64_t pos;
   if (a.seqlens != nullptr) {
     const int64_t total = (int64_t)a.seqlens[b] + 1;
-    if (total < a.L || total > a.capacity) return;  // out-of-range length: batch skipped
+    if (total < a.L || (!a.rolling && total > a.capacity)) return;  // out-of-range length: batch skipped
     pos = total - a.L + l;
   } else {
     pos = a.pos0 + l;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void rotary_kernel(RotaryArgs a) {
   const int i0 = P * c;
   const char* src = reinterpret_cast<const char*>(a.src[j]) +
                     E::kBytes * (b * a.s_sb[j] + h * a.s_sh[j] + (int64_t)l * a.s_ss[j]);
-  const int64_t drow = a.to_slot[j] ? pos : l;
+  const int64_t drow = a.to_slot[j] ? (a.rolling ? pos % a.capacity : pos) : l;
   char* dst = reinterpret_cast<char*>(a.dst[j]) +
               E::kBytes * (b * a.d_sb[j] + h * a.d_sh[j] + drow * a.d_ss[j]);
   float x[P], y[P];
