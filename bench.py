@@ -22,7 +22,8 @@ this host (the oracle as it stands, on a bounded number of full decode
 steps).  `extra` reports the prompt workloads (TFLOP/s against the bf16 MFMA
 peak) and the speculative-decode workload the same way; `rotary` times the
 rotary embedding of the long prompt's Q and K (GB/s against HBM) and a decode
-step's append with rotary beside the plain append.
+step's append with rotary beside the plain append; `rolling` times the
+speculative-decode workload against a rolling cache of W + curr - 1 slots.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
        [--no-cpu-baseline] [--workload NAME]
@@ -297,6 +298,64 @@ def bench_rotary(steps, warmup):
     return res
 
 
+def bench_rolling(reps):
+    """The speculative-decode workload (window 4096, 4 new tokens on a past of
+    16384) against a rolling cache of W + curr - 1 = 4099 slots instead of
+    the 32768-slot linear cache: the same keys are read, from ring slots.
+    Graphs of back-to-back decodes over 8 ring replicas (1 GiB), HIP events
+    around the replays."""
+    import torch
+    from windowed_gqa_kv_amd import binding, work
+    from windowed_gqa_kv_amd.inputs import WORKLOADS, generate
+
+    w = WORKLOADS[4]
+    d = generate(w)
+    C = w.window + w.Lq - 1
+    plan = binding.Plan(w.Hq, w.Hkv, w.D, dtype=w.dtype, scale=w.sm_scale, local_window_size=w.window,
+                        softcap=w.softcap, smooth_softmax=w.smooth_softmax, use_head_sink=w.head_sink,
+                        is_causal=w.causal, rolling_cache=True, max_batch=w.B, max_q_len=w.Lq,
+                        max_kv_len=C)
+    seq = d["seqlens_k"]
+    top = int(seq.max()) + 1
+    # ring slot p mod C holds the cache row of position p, for the last C positions
+    pos = torch.arange(top - C, top)
+    slots = pos % C
+    ring_k = torch.empty(w.B, w.Hkv, C, w.D, dtype=d["k_cache"].dtype)
+    ring_v = torch.empty_like(ring_k)
+    ring_k[:, :, slots] = d["k_cache"][:, :, pos]
+    ring_v[:, :, slots] = d["v_cache"][:, :, pos]
+    R = 8
+    rk, rv = ring_k.cuda(), ring_v.cuda()
+    rings = [(rk.clone(), rv.clone()) for _ in range(R)]
+    del rk, rv, ring_k, ring_v
+    q, seq_d = d["q"].cuda(), seq.cuda()
+    kn, vn = d["k_new"].cuda(), d["v_new"].cuda()
+    sink = None if d["head_sink"] is None else d["head_sink"].cuda()
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(16, plan.workspace_size()), dtype=torch.uint8, device="cuda")
+    for kc, vc in rings:
+        plan.append_kv(kn, vn, kc, vc, seq_d)
+        plan.decode(q, kc, vc, seq_d, out, head_sink=sink, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for kc, vc in rings:
+            plan.decode(q, kc, vc, seq_d, out, head_sink=sink, workspace=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = _events(reps)
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / (reps * R)
+    b = work.decode_bytes(seq.numpy().astype("int64"), w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window)
+    return {"workload": w.name, "ring_slots": C, "linear_capacity": w.Lk, "kernel_ms": round(ms, 5),
+            "achieved": round(b / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
+            "frac": round(b / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(w, d, budget_s=12.0):
     """The float64 oracle on full decode steps of the same workload, repeated
     until ~budget_s of CPU time; reported in the same unit (GB/s)."""
@@ -410,6 +469,7 @@ def main():
             torch.cuda.empty_cache()
         line["extra"] = extra
         line["rotary"] = bench_rotary(args.extra_steps, 3)
+        line["rolling"] = bench_rolling(5)
 
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, r["inputs"])
     print(json.dumps(line), flush=True)
