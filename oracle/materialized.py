@@ -46,6 +46,11 @@ For batch b, query head h, query row i and key slot j:
 6. A row with no allowed key gives exactly 0 ([ALC] "Scheduling, precision,
    and invariants").  Masking is a select, never indicator * sentinel
    ([tract] "On the mask sentinel").
+7. An optional caller mask broadcast over [B, Hq, Lq, Lk] ([ALC] "Layouts
+   and semantics": boolean and float additive broadcast masks): a boolean
+   mask takes the keys where it is False out of the allowed set; an additive
+   mask adds its value to the scaled logit ([tract] "What changed":
+   attention_bias summed with the band).
 
 Readings taken where the pages leave a step open
 ------------------------------------------------
@@ -60,7 +65,11 @@ Readings taken where the pages leave a step open
 * nonpad_kv_seqlen masks keys j >= nonpad_b but does not move q_offset;
 * key slots that no query row of a (batch, head, row-block) may see never
   influence the result, whatever they hold (stale cache slots, padding); a
-  slot that some row may see must hold finite values.
+  slot that some row may see must hold finite values;
+* a boolean mask is True where the query may attend; an additive mask is
+  added to the scaled logit before softcap (scale, bias, cap), a key whose
+  added value is -inf leaves the allowed set (so a row whose every key has
+  -inf is 0), and the sink logit gets no bias.
 """
 
 from __future__ import annotations
@@ -126,14 +135,16 @@ def _check_attrs(Hq, Hkv, causal, window, softcap, scale):
 
 def attention(q, k, v, q_offset, valid, *, scale: float, causal: bool = True,
               window: int = -1, softcap: float = 0.0, sink=None, rows=None,
-              chunk: int = 256):
+              mask=None, chunk: int = 256):
     """Materialized attention over arbitrary per-batch offsets.
 
     q: [B, Hq, Lq, D]; k, v: [B, Hkv, Lk, D]; q_offset, valid: length-B ints.
     ``sink`` is None or a length-Hq array of natural-log logits.  ``rows``
     optionally restricts the computation to those query rows (each row is
     independent, so a subset is the same arithmetic); the result then has
-    len(rows) rows.  Returns float64 [B, Hq, len(rows), D].
+    len(rows) rows.  ``mask`` is None or an array broadcastable to
+    [B, Hq, Lq, Lk]: boolean (True = may attend) or float (added to the
+    scaled logit).  Returns float64 [B, Hq, len(rows), D].
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -147,6 +158,11 @@ def attention(q, k, v, q_offset, valid, *, scale: float, causal: bool = True,
     q_offset = np.broadcast_to(np.asarray(q_offset, dtype=np.int64), (B,))
     valid = np.broadcast_to(np.asarray(valid, dtype=np.int64), (B,))
     rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    if mask is not None:
+        mask = np.asarray(mask)
+        if mask.dtype != np.bool_:
+            mask = mask.astype(np.float64)
+        mask = np.broadcast_to(mask, (B, Hq, Lq, Lk))
     out = np.zeros((B, Hq, rows.shape[0], D), dtype=np.float64)
     j = np.arange(Lk)
     with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
@@ -161,6 +177,11 @@ def attention(q, k, v, q_offset, valid, *, scale: float, causal: bool = True,
                     q_abs = q_offset[b] + r
                     M = allowed(q_abs[:, None], j[None, :], valid[b], causal, window)
                     X = scale * (q[b, h, r] @ kbg.T)
+                    if mask is not None and mask.dtype == np.bool_:
+                        M = M & mask[b, h, r]
+                    elif mask is not None:
+                        M = M & (mask[b, h, r] > -np.inf)
+                        X = X + np.where(M, mask[b, h, r], 0.0)
                     X = softcap_fn(X, softcap)
                     X = np.where(M, X, -np.inf)
                     m = X.max(axis=1)
@@ -182,7 +203,7 @@ def attention(q, k, v, q_offset, valid, *, scale: float, causal: bool = True,
 
 def prefill(q, k, v, *, scale: float, causal: bool = True, window: int = -1,
             softcap: float = 0.0, smooth_softmax: bool = False, head_sink=None,
-            nonpad_kv_seqlen=None, rows=None):
+            nonpad_kv_seqlen=None, rows=None, mask=None):
     """Prompt attention on an empty past: q_offset = Lk - Lq for every batch.
 
     ``nonpad_kv_seqlen`` (length B, 0 <= n <= Lk) masks keys j >= n without
@@ -200,12 +221,12 @@ def prefill(q, k, v, *, scale: float, causal: bool = True, window: int = -1,
     q_offset = np.full(B, Lk - Lq, dtype=np.int64)
     sink = sink_logits(Hq, smooth_softmax, head_sink)
     return attention(q, k, v, q_offset, valid, scale=scale, causal=causal,
-                     window=window, softcap=softcap, sink=sink, rows=rows)
+                     window=window, softcap=softcap, sink=sink, rows=rows, mask=mask)
 
 
 def decode(q, k_cache, v_cache, seqlens_k, *, scale: float, causal: bool = True,
            window: int = -1, softcap: float = 0.0, smooth_softmax: bool = False,
-           head_sink=None, rows=None):
+           head_sink=None, rows=None, mask=None):
     """Decode of curr = q.shape[2] new tokens against a cache already holding them.
 
     seqlens_k[b] = total_b - 1: the newest token sits at slot seqlens_k[b];
@@ -221,7 +242,7 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: float, causal: bool = True,
     sink = sink_logits(Hq, smooth_softmax, head_sink)
     return attention(q, k_cache, v_cache, total - curr, total, scale=scale,
                      causal=causal, window=window, softcap=softcap, sink=sink,
-                     rows=rows)
+                     rows=rows, mask=mask)
 
 
 def append_kv(k_cache, v_cache, k_new, v_new, seqlens_k):
