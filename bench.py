@@ -23,7 +23,9 @@ steps).  `extra` reports the prompt workloads (TFLOP/s against the bf16 MFMA
 peak) and the speculative-decode workload the same way; `rotary` times the
 rotary embedding of the long prompt's Q and K (GB/s against HBM) and a decode
 step's append with rotary beside the plain append; `rolling` times the
-speculative-decode workload against a rolling cache of W + curr - 1 slots.
+speculative-decode workload against a rolling cache of W + curr - 1 slots;
+`masks` times the long prompt through the masked (streaming) kernel with an
+all-True and a block-sparse boolean mask.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
        [--no-cpu-baseline] [--workload NAME]
@@ -356,6 +358,50 @@ def bench_rolling(reps):
             "frac": round(b / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def bench_masks(steps):
+    """The long prompt through gqa_prefill_masked (the streaming kernel, one
+    wavefront per row): an all-True boolean mask (every pair of the band
+    evaluated) and a block-sparse one (about half of the 64-key blocks of
+    every 16-row group cleared, which the kernel skips whole).  FLOPs are
+    4*D per kept pair of band and mask."""
+    import numpy as np
+    import torch
+    from windowed_gqa_kv_amd import binding
+    from windowed_gqa_kv_amd.inputs import WORKLOADS, generate
+
+    w = WORKLOADS[3]
+    d = generate(w)
+    plan = binding.Plan(w.Hq, w.Hkv, w.D, dtype=w.dtype, local_window_size=w.window,
+                        max_batch=w.B, max_q_len=w.Lq, max_kv_len=w.Lk)
+    q, k, v = d["q"].cuda(), d["k"].cuda(), d["v"].cuda()
+    out = torch.empty_like(q)
+    del d
+    i = (w.Lk - w.Lq) + np.arange(w.Lq)[:, None]
+    j = np.arange(w.Lk)[None, :]
+    band = (j <= i) & (i - j < w.window)
+    rng = np.random.default_rng(5)
+    keep = rng.random(((w.Lq + 15) // 16, (w.Lk + 63) // 64)) < 0.5
+    sparse = np.repeat(np.repeat(keep, 16, 0), 64, 1)[:w.Lq, :w.Lk]
+    res = {"workload": w.name, "kernel": "attn_generic_kernel (masked calls)"}
+    for name, m in (("all_true", np.ones((w.Lq, w.Lk), bool)), ("block_sparse", sparse)):
+        md = torch.from_numpy(m)[None, None].cuda()
+        pairs = int((band & m).sum()) * w.B * w.Hq
+        plan.prefill(q, k, v, out, mask=md)
+        evs = _events(steps)
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record()
+            plan.prefill(q, k, v, out, mask=md)
+            b.record()
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+        tf = 4 * w.D * pairs / (ms / 1e3) / 1e12
+        res[name] = {"kernel_ms": round(ms, 4), "kept_pairs": pairs, "achieved": round(tf, 2),
+                     "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del md
+    return res
+
+
 def cpu_baseline(w, d, budget_s=12.0):
     """The float64 oracle on full decode steps of the same workload, repeated
     until ~budget_s of CPU time; reported in the same unit (GB/s)."""
@@ -470,6 +516,7 @@ def main():
         line["extra"] = extra
         line["rotary"] = bench_rotary(args.extra_steps, 3)
         line["rolling"] = bench_rolling(5)
+        line["masks"] = bench_masks(3)
 
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, r["inputs"])
     print(json.dumps(line), flush=True)

@@ -226,6 +226,47 @@ gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr, int64_
                                 const int32_t* seqlens_k, const gqa_rotary_tables* tables,
                                 void* hip_stream);
 
+/* A caller mask over [B, Hq, Lq, Lk] (decode: [B, Hq, curr, capacity], the
+ * key index being the position), broadcast by zero strides ("Attention
+ * Kernel Design", section "Layouts and semantics": boolean and float
+ * additive broadcast masks; "onnx: import GroupQueryAttention decode steps
+ * ...", section "What changed": attention_bias summed with the band).
+ *   GQA_MASK_BOOL: uint8, nonzero = the query may attend the key; the keys it
+ *     clears leave the allowed set.
+ *   GQA_MASK_ADDITIVE: fp32, added to the scaled logit before softcap; -inf
+ *     (or NaN) removes the key; +inf is not allowed.  The sink gets no bias.
+ * A row left with no key is exactly 0.  Device memory, caller-owned; the
+ * key dimension is contiguous, strides are in elements and >= 0. */
+typedef enum { GQA_MASK_BOOL = 1, GQA_MASK_ADDITIVE = 2 } gqa_mask_kind;
+typedef struct {
+  const void* data;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_q;
+  gqa_mask_kind kind;
+} gqa_mask;
+
+/* gqa_prefill with a caller mask (arguments otherwise as gqa_prefill).  Runs
+ * the streaming one-wavefront-per-row kernel: each lane reads the mask entry
+ * of its key, and a 64-key block with no key left is skipped whole (the
+ * all-false block skipping of "Attention Kernel Design", section "Compute
+ * paths"); additive masks are evaluated in full.
+ * Errors: as gqa_prefill, and INVALID_ARG for a NULL mask, an unknown kind or
+ *   a negative stride, UNSUPPORTED for a misaligned additive mask. */
+gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk,
+                              gqa_tensor q, gqa_tensor k, gqa_tensor v, gqa_tensor out,
+                              const int64_t* nonpad_kv_seqlen, const float* head_sink,
+                              const gqa_mask* mask, void* hip_stream);
+
+/* gqa_decode with a caller mask over [B, Hq, curr, capacity] (arguments
+ * otherwise as gqa_decode; no workspace).  Same kernel and rules as
+ * gqa_prefill_masked.  Errors: as gqa_decode and gqa_prefill_masked, and
+ *   UNSUPPORTED with a rolling cache (positions pass the mask's width). */
+gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                             gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache,
+                             gqa_tensor out, const int32_t* seqlens_k, const float* head_sink,
+                             const gqa_mask* mask, void* hip_stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* gqa_last_error(void);
 

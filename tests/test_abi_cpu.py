@@ -204,6 +204,27 @@ def test_rolling_cache_validation():
                                   None) == B.GQA_OK
 
 
+def test_mask_validation():
+    h = plan()
+    s = ctypes.c_void_p(FAKE)
+    ok = B.gqa_mask(FAKE, 0, 0, 1024, B.GQA_MASK_BOOL)
+    def pf(mask, Bn=2, **kw):
+        return B.gqa_prefill_masked(h, Bn, 8, 8, t(), t(), t(), t(), None, None, mask, None)
+    def dc(mask, Bn=2, hh=h):
+        return B.gqa_decode_masked(hh, Bn, 1, 64, t(), t(), t(), t(), s, None, mask, None)
+    assert pf(None) == B.GQA_ERR_INVALID_ARG and "mask" in B.gqa_last_error()
+    assert pf(B.gqa_mask(0, 0, 0, 8, 1)) == B.GQA_ERR_INVALID_ARG and "mask.data" in B.gqa_last_error()
+    assert pf(B.gqa_mask(FAKE, 0, 0, 8, 3)) == B.GQA_ERR_INVALID_ARG and "kind" in B.gqa_last_error()
+    assert pf(B.gqa_mask(FAKE, -1, 0, 8, 1)) == B.GQA_ERR_INVALID_ARG and "negative" in B.gqa_last_error()
+    assert pf(B.gqa_mask(FAKE + 2, 0, 0, 8, 2)) == B.GQA_ERR_UNSUPPORTED and "aligned" in B.gqa_last_error()
+    assert pf(ok, Bn=5) == B.GQA_ERR_CAPACITY
+    assert pf(ok, Bn=0) == B.GQA_OK
+    assert dc(None) == B.GQA_ERR_INVALID_ARG
+    assert dc(ok, Bn=0) == B.GQA_OK
+    hr = plan(rolling_cache=1, local_window_size=8)
+    assert dc(ok, hh=hr) == B.GQA_ERR_UNSUPPORTED and "rolling" in B.gqa_last_error()
+
+
 def test_last_error_is_thread_local_and_specific():
     import threading
     B.gqa_plan(attrs(num_heads=0), 1, 1, 1)

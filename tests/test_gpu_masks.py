@@ -1,0 +1,148 @@
+"""Caller masks on the GPU (gqa_prefill_masked, gqa_decode_masked) against the
+oracle's masked attention, on the same seeded inputs and masks.
+
+Masks are drawn here with their own seeds: boolean masks (True attends) with
+random and block-sparse structure, additive fp32 masks with -inf entries,
+broadcast over batch and/or heads.  Rows that lose every key must be exactly
+zero.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import compare, make_plan
+from windowed_gqa_kv_amd.inputs import Workload, generate, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _bool_mask(seed, shape, keep=0.7):
+    return torch.from_numpy(np.random.default_rng(seed).random(shape) < keep)
+
+
+def _add_mask(seed, shape, neg_inf=0.05):
+    rng = np.random.default_rng(seed)
+    m = (rng.standard_normal(shape) * 2.0).astype(np.float32)
+    m[rng.random(shape) < neg_inf] = -np.inf
+    return torch.from_numpy(m)
+
+
+def _block_sparse(seed, Lq, Lk, block=64):
+    """Whole 64-key blocks cleared per 16-row group, about half of them."""
+    rng = np.random.default_rng(seed)
+    keep = rng.random(((Lq + 15) // 16, (Lk + block - 1) // block)) < 0.5
+    m = np.repeat(np.repeat(keep, 16, 0), block, 1)[:Lq, :Lk]
+    return torch.from_numpy(m[None, None])
+
+
+PREFILL = [
+    # (dtype, B, Hq, Hkv, D, Lq, Lk, window, softcap, sink, nonpad, mask kind, mask shape)
+    ("bf16", 2, 8, 2, 128, 200, 200, 64, 0.0, True, (200, 150), "bool", "b1"),
+    ("bf16", 2, 8, 2, 128, 130, 257, -1, 0.0, False, None, "add", "1h"),
+    ("f16", 1, 4, 4, 64, 96, 96, -1, 30.0, True, None, "add", "bh"),
+    ("f32", 1, 4, 2, 32, 64, 64, 16, 0.0, True, None, "bool", "11"),
+    ("bf16", 1, 8, 2, 128, 300, 300, -1, 0.0, False, None, "sparse", "11"),
+    ("f32", 2, 4, 2, 64, 70, 90, 20, 5.0, False, (90, 33), "add", "b1"),
+]
+
+
+def _shape(tag, B, Hq, Lq, Lk):
+    return {"b1": (B, 1, Lq, Lk), "1h": (1, Hq, Lq, Lk), "bh": (B, Hq, Lq, Lk), "11": (1, 1, Lq, Lk)}[tag]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: f"{c[0]}_D{c[4]}_{c[11]}_{c[12]}_W{c[7]}")
+def test_masked_prefill_matches_oracle(gpu, case):
+    dtype, B, Hq, Hkv, D, Lq, Lk, W, cap, sink, nonpad, kind, tag = case
+    w = Workload("mask", "prefill", dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, Lq=Lq, Lk=Lk, window=W,
+                 softcap=cap, head_sink=sink, nonpad=nonpad, value_scale=0.5, seed=300 + D + Lq)
+    d = generate(w)
+    shape = _shape(tag, B, Hq, Lq, Lk)
+    if kind == "bool":
+        mask = _bool_mask(Lq * 7 + Lk, shape)
+        mask[..., 3, :] = False  # a row with no key left
+    elif kind == "sparse":
+        mask = _block_sparse(Lq, Lq, Lk)
+    else:
+        mask = _add_mask(Lq * 11 + Lk, shape)
+        mask[..., 5, :] = -np.inf  # a row with no key left
+    plan = make_plan(w)
+    out = plan.prefill(d["q"].cuda(), d["k"].cuda(), d["v"].cuda(), mask=mask.cuda(),
+                       nonpad_kv_seqlen=None if d["nonpad"] is None else d["nonpad"].cuda(),
+                       head_sink=None if d["head_sink"] is None else d["head_sink"].cuda())
+    torch.cuda.synchronize()
+    want = oracle.prefill(to_f64(d["q"]), to_f64(d["k"]), to_f64(d["v"]), scale=w.sm_scale, window=W,
+                          softcap=cap, head_sink=to_f64(d["head_sink"]),
+                          nonpad_kv_seqlen=None if d["nonpad"] is None else d["nonpad"].numpy(),
+                          mask=mask.numpy() if kind != "add" else mask.numpy().astype(np.float64))
+    compare(out, want, dtype, f"masked prefill {case}")
+    if kind in ("bool", "add"):
+        row = 3 if kind == "bool" else 5
+        assert not out[:, :, row].any(), "a row with every key masked must be zero"
+
+
+@pytest.mark.parametrize("dtype,D,curr,cap,kind", [("bf16", 128, 1, 1024, "bool"),
+                                                    ("bf16", 256, 4, 600, "add"),
+                                                    ("f32", 32, 2, 100, "bool")])
+def test_masked_decode_matches_oracle(gpu, dtype, D, curr, cap, kind):
+    B, Hq, Hkv = 3, 8, 2
+    seq = [cap - 1, 17, cap // 2]
+    w = Workload("maskdec", "decode", dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, Lq=curr, Lk=cap,
+                 window=-1 if D != 256 else 200, softcap=50.0 if D == 256 else 0.0,
+                 smooth_softmax=True, seqlens=("list", seq), seed=400 + D + curr)
+    d = generate(w)
+    shape = (B, Hq, curr, cap)
+    mask = _bool_mask(D + cap, shape, 0.6) if kind == "bool" else _add_mask(D + cap, shape)
+    plan = make_plan(w)
+    kc, vc = d["k_cache"].cuda(), d["v_cache"].cuda()
+    seq_d = d["seqlens_k"].cuda()
+    plan.append_kv(d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, seq_d)
+    out = plan.decode(d["q"].cuda(), kc, vc, seq_d, mask=mask.cuda())
+    torch.cuda.synchronize()
+    s = d["seqlens_k"].numpy().astype(np.int64)
+    kc_o, vc_o = oracle.append_kv(to_f64(d["k_cache"]), to_f64(d["v_cache"]), to_f64(d["k_new"]),
+                                  to_f64(d["v_new"]), s)
+    want = oracle.decode(to_f64(d["q"]), kc_o, vc_o, s, scale=w.sm_scale, window=w.window,
+                         softcap=w.softcap, smooth_softmax=True,
+                         mask=mask.numpy() if kind == "bool" else mask.numpy().astype(np.float64))
+    compare(out, want, dtype, f"masked decode {dtype} D={D} curr={curr}")
+
+
+def test_all_true_mask_equals_the_unmasked_kernels(gpu):
+    """An all-True boolean mask through the masked (streaming) kernel against
+    the matrix-core prefill without a mask: both within tolerance of the
+    oracle, and of each other."""
+    w = Workload("masktrue", "prefill", "bf16", B=1, Hq=8, Hkv=2, D=128, Lq=256, Lk=256, window=100,
+                 head_sink=True, value_scale=0.5, seed=77)
+    d = generate(w)
+    plan = make_plan(w)
+    q, k, v, sk = d["q"].cuda(), d["k"].cuda(), d["v"].cuda(), d["head_sink"].cuda()
+    a = plan.prefill(q, k, v, head_sink=sk, mask=torch.ones(1, 1, 256, 256, dtype=torch.bool, device="cuda"))
+    b = plan.prefill(q, k, v, head_sink=sk)
+    torch.cuda.synchronize()
+    want = oracle.prefill(to_f64(d["q"]), to_f64(d["k"]), to_f64(d["v"]), scale=w.sm_scale, window=100,
+                          head_sink=to_f64(d["head_sink"]))
+    compare(a, want, "bf16", "all-true mask")
+    compare(b, want, "bf16", "no mask")
+
+
+def test_masked_prefill_full_size_sampled(gpu):
+    """The long prompt (32 heads x 8192 rows, window 4096) with a block-sparse
+    boolean mask, as the benchmark runs it; sampled rows against the oracle."""
+    from windowed_gqa_kv_amd.inputs import WORKLOADS
+    w = WORKLOADS[3]
+    d = generate(w)
+    mask = _block_sparse(5, w.Lq, w.Lk)
+    plan = make_plan(w)
+    out = plan.prefill(d["q"].cuda(), d["k"].cuda(), d["v"].cuda(), mask=mask.cuda())
+    torch.cuda.synchronize()
+    rows = np.r_[0:3, 4093:4099, 8189:8192, np.random.default_rng(9).integers(0, 8192, 8)]
+    heads = [0, 13, 31]
+    G = w.Hq // w.Hkv
+    for h in heads:
+        g = h // G
+        want = oracle.prefill(to_f64(d["q"][:, h:h + 1]), to_f64(d["k"][:, g:g + 1]),
+                              to_f64(d["v"][:, g:g + 1]), scale=w.sm_scale, window=w.window,
+                              rows=rows, mask=mask.numpy())
+        compare(out[:, h:h + 1, rows], want, "bf16", f"full-size masked head {h}")

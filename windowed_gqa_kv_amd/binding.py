@@ -32,7 +32,8 @@ DTYPE_CODES = {"f32": GQA_F32, "f16": GQA_F16, "bf16": GQA_BF16}
 
 EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
-            "gqa_last_error")
+            "gqa_prefill_masked", "gqa_decode_masked", "gqa_last_error")
+GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
 class gqa_attrs(ctypes.Structure):
@@ -68,6 +69,16 @@ class gqa_rotary_tables(ctypes.Structure):
     ]
 
 
+class gqa_mask(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_q", ctypes.c_int64),
+        ("kind", ctypes.c_int),
+    ]
+
+
 gqa_plan_t = ctypes.c_void_p
 _lib = None
 
@@ -99,6 +110,11 @@ def load():
     lib.gqa_apply_rotary.restype = ctypes.c_int
     lib.gqa_append_kv_rotary.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, T, T, P, RT, P]
     lib.gqa_append_kv_rotary.restype = ctypes.c_int
+    MK = ctypes.POINTER(gqa_mask)
+    lib.gqa_prefill_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, MK, P]
+    lib.gqa_prefill_masked.restype = ctypes.c_int
+    lib.gqa_decode_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, MK, P]
+    lib.gqa_decode_masked.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -150,6 +166,17 @@ def gqa_append_kv_rotary(plan, B, curr, capacity, q, q_rot, k_new, v_new, k_cach
     return load().gqa_append_kv_rotary(plan, B, curr, capacity, q, q_rot, k_new, v_new, k_cache,
                                        v_cache, seqlens_k,
                                        None if tables is None else ctypes.byref(tables), stream)
+
+
+def gqa_prefill_masked(plan, B, Lq, Lk, q, k, v, out, nonpad_kv_seqlen, head_sink, mask, stream) -> int:
+    return load().gqa_prefill_masked(plan, B, Lq, Lk, q, k, v, out, nonpad_kv_seqlen, head_sink,
+                                     None if mask is None else ctypes.byref(mask), stream)
+
+
+def gqa_decode_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, mask,
+                      stream) -> int:
+    return load().gqa_decode_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
+                                    head_sink, None if mask is None else ctypes.byref(mask), stream)
 
 
 def gqa_last_error() -> str:
@@ -248,9 +275,27 @@ class Plan:
             if t is not None and _dtype_code(t) != want:
                 raise TypeError(f"tensor dtype {t.dtype} does not match the plan's {self.dtype}")
 
+    def mask_view(self, mask, B, Lq, Lk) -> gqa_mask:
+        """gqa_mask for a bool (True attends) or float32 (additive) tensor
+        broadcastable to [B, Hq, Lq, Lk]."""
+        import torch
+        if mask.dim() != 4:
+            raise ValueError("a mask is 4-D, broadcastable to [B, Hq, Lq, Lk]")
+        m = mask.expand(B, self.num_heads, Lq, Lk)
+        if m.stride(3) != 1 and Lk > 1:
+            raise ValueError("the mask's key dimension must be contiguous")
+        if mask.dtype == torch.bool:
+            kind = GQA_MASK_BOOL
+        elif mask.dtype == torch.float32:
+            kind = GQA_MASK_ADDITIVE
+        else:
+            raise TypeError("a mask is bool (True attends) or float32 (additive)")
+        return gqa_mask(m.data_ptr(), m.stride(0), m.stride(1), m.stride(2), kind)
+
     def prefill(self, q, k, v, out=None, *, nonpad_kv_seqlen=None, head_sink=None,
-                layout="bhsd", stream=None):
-        """q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (layout "bhsd") or [B,L,H*D] ("bshd")."""
+                layout="bhsd", mask=None, stream=None):
+        """q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (layout "bhsd") or [B,L,H*D] ("bshd").
+        ``mask``: bool or float32, broadcastable to [B, Hq, Lq, Lk]."""
         import torch
         self._check_dtype(q, k, v)
         if out is None:
@@ -264,6 +309,11 @@ class Plan:
             Lk = k.shape[1]
             qv, ov = tensor_view(q, self.num_heads), tensor_view(out, self.num_heads)
             kv_, vv = tensor_view(k, self.kv_num_heads), tensor_view(v, self.kv_num_heads)
+        if mask is not None:
+            check(gqa_prefill_masked(self._h, B, Lq, Lk, qv, kv_, vv, ov, _ptr(nonpad_kv_seqlen),
+                                     _ptr(head_sink), self.mask_view(mask, B, Lq, Lk),
+                                     _stream(stream)))
+            return out
         check(gqa_prefill(self._h, B, Lq, Lk, qv, kv_, vv, ov, _ptr(nonpad_kv_seqlen),
                           _ptr(head_sink), None, 0, _stream(stream)))
         return out
@@ -276,11 +326,20 @@ class Plan:
                             _ptr(seqlens_k), _stream(stream)))
 
     def decode(self, q, k_cache, v_cache, seqlens_k, out=None, *, head_sink=None,
-               workspace=None, stream=None):
+               workspace=None, mask=None, stream=None):
+        """``mask``: bool or float32, broadcastable to [B, Hq, curr, capacity]."""
         import torch
         self._check_dtype(q, k_cache, v_cache)
         if out is None:
             out = torch.empty_like(q)
+        if mask is not None:
+            B, _, curr, _ = q.shape
+            check(gqa_decode_masked(self._h, B, curr, k_cache.shape[2], tensor_view(q),
+                                    tensor_view(k_cache), tensor_view(v_cache), tensor_view(out),
+                                    _ptr(seqlens_k), _ptr(head_sink),
+                                    self.mask_view(mask, B, curr, k_cache.shape[2]),
+                                    _stream(stream)))
+            return out
         if workspace is None:
             workspace = self.new_workspace(q.device)
         B, _, curr, _ = q.shape

@@ -8,7 +8,11 @@
 // of "Attention Kernel Design", section "Compute paths"; accumulation is fp32
 // and only the final output is narrowed (section "Scheduling, precision, and
 // invariants").  It serves fp32, head sizes the MFMA kernels do not cover,
-// and any row count.
+// any row count, and calls with a caller mask (boolean or additive, "Attention
+// Kernel Design", sections "Layouts and semantics" and "Compute paths"): each
+// lane reads the mask entry of its key, and a 64-key block in which no key is
+// left is skipped whole (no K or V reads), the all-false block skipping of
+// the streaming path.
 #include "kernels.h"
 
 namespace gqa {
@@ -68,10 +72,26 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};  // head dims lane + 64 c
   float m = -INFINITY, l = 0.0f;
+  bool seen = false;  // some key of the row was kept
+  const int64_t m_row = b * a.m_sb + h * a.m_sh + (int64_t)i * a.m_sq;
   for (int kb = lo; kb <= hi; kb += 64) {
     const int j = kb + lane;
+    bool keep = j <= hi;
+    float bias = 0.0f;
+    if (a.mask_kind != 0) {
+      if (keep) {
+        if (a.mask_kind == 1) {
+          keep = reinterpret_cast<const uint8_t*>(a.mask)[m_row + j] != 0;
+        } else {
+          bias = reinterpret_cast<const float*>(a.mask)[m_row + j];
+          keep = bias > -INFINITY;
+        }
+      }
+      if (__ballot(keep) == 0) continue;  // no key left in this block: skip it
+    }
+    seen = true;
     float t = -INFINITY;
-    if (j <= hi) {
+    if (keep) {
       float dot = 0.0f;
       for (int d0 = 0; d0 < a.D; d0 += 8) {
         float kx[8], qx[8];
@@ -80,17 +100,19 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot = fmaf(qx[e], kx[e], dot);
       }
-      t = capped ? a.cap_log2 * tanh_f32(dot * a.scale_over_cap) : dot * a.scale_log2;
+      t = capped ? a.cap_log2 * tanh_f32(dot * a.scale_over_cap + bias * a.inv_cap)
+                 : dot * a.scale_log2 + bias * kLog2e;
     }
     const float m_new = fmaxf(m, wave_max(t));  // finite: the block holds >= 1 key
     const float alpha = fast_exp2(m - m_new);    // 0 on the first block
-    const float pj = (j <= hi) ? fast_exp2(t - m_new) : 0.0f;
+    const float pj = keep ? fast_exp2(t - m_new) : 0.0f;
     l = l * alpha + wave_sum(pj);
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] *= alpha;
     const int nk = min(64, hi - kb + 1);
     for (int jj = 0; jj < nk; ++jj) {
       const float pv = __shfl(pj, jj, 64);
+      if (a.mask_kind != 0 && pv == 0.0f) continue;  // a masked key (wave-uniform)
       const int64_t vrow = v_base + (int64_t)slot_of(a, kb + jj) * a.v_ss;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -102,7 +124,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   }
 
   float fac;
-  if (lo > hi) {
+  if (lo > hi || !seen) {
     fac = 0.0f;  // no allowed key: exactly zero, with or without a sink
   } else if (a.use_sink) {
     const float ts = sink_log2(a, h);

@@ -92,6 +92,7 @@ gqa::AttnArgs make_args(const gqa_plan_s* p, const gqa_tensor& q, const gqa_tens
   a.scale_log2 = p->scale * log2e;
   a.scale_over_cap = p->attrs.softcap > 0 ? p->scale / p->attrs.softcap : 0.0f;
   a.cap_log2 = p->attrs.softcap > 0 ? p->attrs.softcap * log2e : 0.0f;
+  a.inv_cap = p->attrs.softcap > 0 ? 1.0f / p->attrs.softcap : 0.0f;
   return a;
 }
 
@@ -398,6 +399,89 @@ GQA_API gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr
   a.max_pos = tables->max_pos;
   return hip_status(gqa::launch_rotary(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
                     "append_kv_rotary launch");
+}
+
+namespace {
+
+gqa_status set_mask(gqa::AttnArgs& a, const gqa_mask* m) {
+  if (m == nullptr) return fail(GQA_ERR_INVALID_ARG, "mask is NULL");
+  if (m->data == nullptr) return fail(GQA_ERR_INVALID_ARG, "mask.data is NULL");
+  if (m->kind != GQA_MASK_BOOL && m->kind != GQA_MASK_ADDITIVE)
+    return fail(GQA_ERR_INVALID_ARG, "mask.kind %d is not GQA_MASK_BOOL or GQA_MASK_ADDITIVE", (int)m->kind);
+  if (m->stride_b < 0 || m->stride_h < 0 || m->stride_q < 0)
+    return fail(GQA_ERR_INVALID_ARG, "mask has a negative stride");
+  if (m->kind == GQA_MASK_ADDITIVE && reinterpret_cast<uintptr_t>(m->data) % 4 != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "an additive mask must be 4-byte aligned");
+  a.mask = m->data;
+  a.m_sb = m->stride_b;
+  a.m_sh = m->stride_h;
+  a.m_sq = m->stride_q;
+  a.mask_kind = (int32_t)m->kind;
+  return GQA_OK;
+}
+
+}  // namespace
+
+GQA_API gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk, gqa_tensor q,
+                                      gqa_tensor k, gqa_tensor v, gqa_tensor out,
+                                      const int64_t* nonpad_kv_seqlen, const float* head_sink,
+                                      const gqa_mask* mask, void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || Lq < 0 || Lk < 0) return fail(GQA_ERR_INVALID_ARG, "B, Lq and Lk must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (Lq > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "Lq = %d exceeds the plan's max_q_len %d", Lq, plan->max_q_len);
+  if (Lk > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "Lk = %lld exceeds the plan's max_kv_len %lld", (long long)Lk,
+                (long long)plan->max_kv_len);
+  gqa_status st = check_sink(plan, head_sink);
+  if (st != GQA_OK) return st;
+  gqa::AttnArgs a = make_args(plan, q, k, v, out, B, Lq, Lk, 0);
+  if ((st = set_mask(a, mask)) != GQA_OK) return st;
+  if (B == 0 || Lq == 0) return GQA_OK;
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("q", q, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
+  if (Lk > 0) {
+    if ((st = check_tensor("k", k, esz)) != GQA_OK) return st;
+    if ((st = check_tensor("v", v, esz)) != GQA_OK) return st;
+  }
+  a.nonpad = nonpad_kv_seqlen;
+  a.head_sink = head_sink;
+  return hip_status(gqa::launch_attn_generic(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
+                    "masked prefill launch");
+}
+
+GQA_API gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                                     gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                     const int32_t* seqlens_k, const float* head_sink, const gqa_mask* mask,
+                                     void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (curr > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the plan's max_q_len %d", curr, plan->max_q_len);
+  if (capacity > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
+                (long long)plan->max_kv_len);
+  if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  if (plan->attrs.rolling_cache)
+    return fail(GQA_ERR_UNSUPPORTED, "a decode mask indexes keys by position: not with a rolling cache");
+  gqa_status st = check_sink(plan, head_sink);
+  if (st != GQA_OK) return st;
+  gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
+  if ((st = set_mask(a, mask)) != GQA_OK) return st;
+  if (B == 0 || curr == 0) return GQA_OK;
+  if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("q", q, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
+  a.seqlens = seqlens_k;
+  a.head_sink = head_sink;
+  return hip_status(gqa::launch_attn_generic(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
+                    "masked decode launch");
 }
 
 GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }
