@@ -359,10 +359,12 @@ def bench_rolling(reps):
 
 
 def bench_masks(steps):
-    """The long prompt through gqa_prefill_masked (the streaming kernel, one
-    wavefront per row): an all-True boolean mask (every pair of the band
-    evaluated) and a block-sparse one (about half of the 64-key blocks of
-    every 16-row group cleared, which the kernel skips whole).  FLOPs are
+    """The long prompt through gqa_prefill_masked with a boolean [1, 1, Lq, Lk]
+    mask (the matrix-core prefill, reading the mask bytes one tile ahead): an
+    all-True mask (every pair of the band evaluated) and a block-sparse one
+    (about half of the 64-key blocks of every 16-row group cleared; a wave
+    skips a tile its 32 rows all lose); and the same block-sparse mask as an
+    additive 0 / -inf mask, which the streaming kernel evaluates.  FLOPs are
     4*D per kept pair of band and mask."""
     import numpy as np
     import torch
@@ -382,9 +384,12 @@ def bench_masks(steps):
     rng = np.random.default_rng(5)
     keep = rng.random(((w.Lq + 15) // 16, (w.Lk + 63) // 64)) < 0.5
     sparse = np.repeat(np.repeat(keep, 16, 0), 64, 1)[:w.Lq, :w.Lk]
-    res = {"workload": w.name, "kernel": "attn_generic_kernel (masked calls)"}
-    for name, m in (("all_true", np.ones((w.Lq, w.Lk), bool)), ("block_sparse", sparse)):
+    res = {"workload": w.name}
+    add = np.where(sparse, 0.0, -np.inf).astype(np.float32)
+    for name, m in (("all_true", np.ones((w.Lq, w.Lk), bool)), ("block_sparse", sparse),
+                    ("block_sparse_additive", add)):
         md = torch.from_numpy(m)[None, None].cuda()
+        m = m if m.dtype == bool else m > -np.inf
         pairs = int((band & m).sum()) * w.B * w.Hq
         plan.prefill(q, k, v, out, mask=md)
         evs = _events(steps)
@@ -396,7 +401,8 @@ def bench_masks(steps):
         torch.cuda.synchronize()
         ms = sum(a.elapsed_time(b) for a, b in evs) / steps
         tf = 4 * w.D * pairs / (ms / 1e3) / 1e12
-        res[name] = {"kernel_ms": round(ms, 4), "kept_pairs": pairs, "achieved": round(tf, 2),
+        res[name] = {"kernel": "prefill_mfma_kernel" if md.dtype == torch.bool else "attn_generic_kernel",
+                     "kernel_ms": round(ms, 4), "kept_pairs": pairs, "achieved": round(tf, 2),
                      "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
         del md
     return res

@@ -37,8 +37,14 @@ def _block_sparse(seed, Lq, Lk, block=64):
     return torch.from_numpy(m[None, None])
 
 
+# Boolean masks with 8-byte-aligned rows (Lk % 8 == 0 here), bf16/f16, head
+# size 64 or 128 and no softcap run on the matrix-core prefill; the others on
+# the streaming kernel.  Both kinds of case are listed.
 PREFILL = [
     # (dtype, B, Hq, Hkv, D, Lq, Lk, window, softcap, sink, nonpad, mask kind, mask shape)
+    ("bf16", 1, 8, 2, 128, 300, 320, -1, 0.0, False, None, "sparse", "11"),   # matrix core
+    ("f16", 2, 4, 4, 64, 130, 264, 100, 0.0, True, (264, 100), "bool", "bh"),  # matrix core
+    ("bf16", 2, 16, 2, 128, 96, 1000, 300, 0.0, False, None, "bool", "1h"),    # matrix core, Lq < Lk
     ("bf16", 2, 8, 2, 128, 200, 200, 64, 0.0, True, (200, 150), "bool", "b1"),
     ("bf16", 2, 8, 2, 128, 130, 257, -1, 0.0, False, None, "add", "1h"),
     ("f16", 1, 4, 4, 64, 96, 96, -1, 30.0, True, None, "add", "bh"),
@@ -64,6 +70,7 @@ def test_masked_prefill_matches_oracle(gpu, case):
         mask[..., 3, :] = False  # a row with no key left
     elif kind == "sparse":
         mask = _block_sparse(Lq, Lq, Lk)
+        mask[..., 7, :] = False  # a row with no key left
     else:
         mask = _add_mask(Lq * 11 + Lk, shape)
         mask[..., 5, :] = -np.inf  # a row with no key left
@@ -77,8 +84,8 @@ def test_masked_prefill_matches_oracle(gpu, case):
                           nonpad_kv_seqlen=None if d["nonpad"] is None else d["nonpad"].numpy(),
                           mask=mask.numpy() if kind != "add" else mask.numpy().astype(np.float64))
     compare(out, want, dtype, f"masked prefill {case}")
-    if kind in ("bool", "add"):
-        row = 3 if kind == "bool" else 5
+    if kind in ("bool", "add", "sparse"):
+        row = {"bool": 3, "add": 5, "sparse": 7}[kind]
         assert not out[:, :, row].any(), "a row with every key masked must be zero"
 
 
@@ -110,9 +117,8 @@ def test_masked_decode_matches_oracle(gpu, dtype, D, curr, cap, kind):
 
 
 def test_all_true_mask_equals_the_unmasked_kernels(gpu):
-    """An all-True boolean mask through the masked (streaming) kernel against
-    the matrix-core prefill without a mask: both within tolerance of the
-    oracle, and of each other."""
+    """An all-True boolean mask through the masked matrix-core prefill against
+    the same kernel without a mask: both within tolerance of the oracle."""
     w = Workload("masktrue", "prefill", "bf16", B=1, Hq=8, Hkv=2, D=128, Lq=256, Lk=256, window=100,
                  head_sink=True, value_scale=0.5, seed=77)
     d = generate(w)

@@ -448,8 +448,18 @@ GQA_API gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, in
   }
   a.nonpad = nonpad_kv_seqlen;
   a.head_sink = head_sink;
-  return hip_status(gqa::launch_attn_generic(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
-                    "masked prefill launch");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int dtype = (int)plan->attrs.dtype;
+  // Boolean masks whose rows are 8-byte aligned run on the matrix-core kernel
+  // (it reads 8 mask bytes per aligned run of keys); anything else (additive
+  // masks, softcap, other layouts) on the streaming kernel.
+  const bool small_strides = a.k_ss < (int64_t(1) << 24) && a.v_ss < (int64_t(1) << 24);
+  const bool aligned8 = reinterpret_cast<uintptr_t>(mask->data) % 8 == 0 && mask->stride_b % 8 == 0 &&
+                        mask->stride_h % 8 == 0 && mask->stride_q % 8 == 0;
+  if (Lk > 0 && small_strides && gqa::prefill_mfma_supported(dtype, plan->attrs.head_size) &&
+      plan->attrs.softcap == 0.0f && mask->kind == GQA_MASK_BOOL && aligned8)
+    return hip_status(gqa::launch_prefill_mfma(a, dtype, false, stream), "masked prefill launch");
+  return hip_status(gqa::launch_attn_generic(a, dtype, stream), "masked prefill launch");
 }
 
 GQA_API gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,

@@ -192,8 +192,15 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Caller-mask bytes are read through global-address-space pointers: generic
+// (flat) loads would also count against lgkmcnt, which the LDS operand reads
+// wait on by count.
+typedef __attribute__((address_space(1))) const uint64_t global_u64;
+typedef __attribute__((address_space(1))) const unsigned char global_u8;
+
 // Two waves per SIMD (two workgroups per CU): the register budget is 256.
-template <bool IS_BF16, int D, bool SOFTCAP>
+// MASK = 1: a caller boolean mask (uint8, nonzero attends) over [B, Hq, Lq, Lk].
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     AttnArgs a, int nrb, int items, int per_xcd, int hw) {
   constexpr int KS = D / 16;    // k-steps of the QK^T contraction
@@ -228,7 +235,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const BatchSpan sp = batch_span(a, b);
   const int row0 = rb * rpw;
   const int rows_here = min(rpw, a.Lq - row0);
-  const int kv_lo = row_lo(a, sp.q_off + row0);
+  // With a caller mask the first tile starts at a multiple of 64 keys, so that
+  // the mask runs below are aligned (keys before the band are masked like any
+  // other excluded key).
+  const int kv_lo = MASK ? (row_lo(a, sp.q_off + row0) & ~(BN - 1)) : row_lo(a, sp.q_off + row0);
   const int kv_hi = row_hi(a, sp.q_off + row0 + rows_here - 1, sp.valid);
 
   const int wrow0 = row0 + 32 * (w / hw);
@@ -308,6 +318,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   static_assert(NDMA >= 1 && NDMA <= KS / 2, "at most one DMA pair per batch of QK operand reads");
 
   const float c_l2 = SOFTCAP ? 1.0f : a.scale_log2;  // raw units -> log2 units
+
+  // ---- caller mask, one tile ahead ----
+  // Per tile, this lane's row holds four runs of 8 keys: run x = 2 s + r is
+  // keys kb + 16 x + 8 h2 .. + 7, the keys of sc[s][8 r .. 8 r + 7].  Masked
+  // tiles start at multiples of 64 keys and the host checks the mask's
+  // alignment, so a run is one aligned 8-byte load; a run that crosses Lk is
+  // read byte by byte.  Rows past Lq read the last row (never stored).
+  global_u8* mrow = nullptr;
+  if constexpr (MASK == 1)
+    mrow = (global_u8*)(reinterpret_cast<const unsigned char*>(a.mask) + b * a.m_sb + h * a.m_sh +
+                        (int64_t)min(my_row, a.Lq - 1) * a.m_sq);
+  auto mask_load = [&](int kb, uint64_t (&mk)[4]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int s0 = kb + 16 * x + 8 * h2;
+      if (s0 + 8 <= a.Lk) {
+        mk[x] = *(global_u64*)(mrow + s0);
+      } else {
+        uint64_t v = 0;
+        for (int e = 0; e < 8; ++e)
+          if (s0 + e < a.Lk) v |= (uint64_t)mrow[s0 + e] << (8 * e);
+        mk[x] = v;
+      }
+    }
+  };
+  uint64_t mk_cur[4] = {0, 0, 0, 0}, mk_nxt[4] = {0, 0, 0, 0};
   const int kr0 = key_of_m(n);                        // this lane's K row in a sub-tile
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0];
@@ -401,6 +437,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           acc[r2] = (j < my_lo || j > my_hi) ? -INFINITY : acc[r2];
         }
       }
+      if constexpr (MASK == 1) {  // the caller mask, on every tile
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) {
+          const uint64_t run = mk_cur[2 * sub + (r2 >> 3)];
+          acc[r2] = ((run >> (8 * (r2 & 7))) & 0xffu) ? acc[r2] : -INFINITY;
+        }
+      }
 #pragma unroll
       for (int r2 = 0; r2 < 16; ++r2) bm = fmaxf(bm, acc[r2]);
     }
@@ -487,7 +530,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // ---- schedule: per tile, K Q^T (the next tile's loads riding along), the
   // softmax, P V; then wait for the next tile and meet ----
   if (nblk > 0) dma_tile(kv_lo, 0);
-  __builtin_amdgcn_s_waitcnt(0);  // Q registers and the first tile
+  if constexpr (MASK == 1)
+    if (nblk > 0) mask_load(kv_lo, mk_nxt);
+  __builtin_amdgcn_s_waitcnt(0);  // Q registers, the first tile (and its mask)
   tile_barrier();
 
   f32x16 sc[2];
@@ -506,6 +551,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     };
     bool a0, a1;
     active(kb, a0, a1);
+    if constexpr (MASK == 1) {
+      // this tile's mask landed with the last tile's loads; fetch the next
+      // one, and skip sub-tiles whose keys the mask clears for all 32 rows
+#pragma unroll
+      for (int x = 0; x < 4; ++x) mk_cur[x] = mk_nxt[x];
+      if (next) mask_load(kb + BN, mk_nxt);
+      a0 = a0 && __any((mk_cur[0] | mk_cur[1]) != 0);
+      a1 = a1 && __any((mk_cur[2] | mk_cur[3]) != 0);
+    }
     if (a0 || a1) {
       qk(stage_tag, sc, dma_at);
       float alpha;
@@ -530,8 +584,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   if (my_row >= a.Lq) return;
   const float l_row = l_run + xor32(l_run);
   float fac;
-  if (my_lo > my_hi) {
-    fac = 0.0f;
+  if (my_lo > my_hi || (MASK != 0 && m_run == -INFINITY)) {
+    fac = 0.0f;  // no key left for the row: exactly zero
   } else if (a.use_sink) {
     const float mt = m_run * c_l2;
     const float ts = sink_log2(a, h);
@@ -555,6 +609,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 template <bool IS_BF16, int D>
 hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
+  if (a.mask_kind != 0 && (softcap || a.mask_kind != 1)) return hipErrorInvalidValue;
   // heads per workgroup: the largest power of two that divides G, at most 8
   const int hw = std::min(a.G & -a.G, kWaves);
   const int rpw = 32 * (kWaves / hw);
@@ -562,10 +617,12 @@ hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
   const int items = a.B * a.Hkv * (a.G / hw) * nrb;
   const int per_xcd = (items + 7) / 8;
   dim3 grid(8 * per_xcd), block(64 * kWaves);
-  if (softcap)
-    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, true>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
+  if (a.mask_kind == 1)
+    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false, 1>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
+  else if (softcap)
+    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, true, 0>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
+    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false, 0>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
   return hipGetLastError();
 }
 
