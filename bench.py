@@ -364,8 +364,8 @@ def bench_masks(steps):
     all-True mask (every pair of the band evaluated) and a block-sparse one
     (about half of the 64-key blocks of every 16-row group cleared; a wave
     skips a tile its 32 rows all lose); and the same block-sparse mask as an
-    additive 0 / -inf mask, which the streaming kernel evaluates.  FLOPs are
-    4*D per kept pair of band and mask."""
+    additive 0 / -inf mask, evaluated in full.  FLOPs are 4*D per kept pair
+    of band and mask."""
     import numpy as np
     import torch
     from windowed_gqa_kv_amd import binding
@@ -401,7 +401,7 @@ def bench_masks(steps):
         torch.cuda.synchronize()
         ms = sum(a.elapsed_time(b) for a, b in evs) / steps
         tf = 4 * w.D * pairs / (ms / 1e3) / 1e12
-        res[name] = {"kernel": "prefill_mfma_kernel" if md.dtype == torch.bool else "attn_generic_kernel",
+        res[name] = {"kernel": "prefill_mfma_kernel",
                      "kernel_ms": round(ms, 4), "kept_pairs": pairs, "achieved": round(tf, 2),
                      "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
         del md

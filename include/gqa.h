@@ -246,14 +246,16 @@ typedef struct {
   gqa_mask_kind kind;
 } gqa_mask;
 
-/* gqa_prefill with a caller mask (arguments otherwise as gqa_prefill).  A
- * boolean mask whose data and strides are multiples of 8 bytes, on a bf16 or
- * fp16 plan of head size 64 or 128 without softcap, runs on the matrix-core
- * prefill: each wave reads its rows' mask bytes one 64-key tile ahead and
- * skips a tile the mask clears for all its 32 rows.  Other masks run on the
- * streaming one-wavefront-per-row kernel, which skips a 64-key block with no
- * key left (the all-false block skipping of "Attention Kernel Design",
- * section "Compute paths"); additive masks are evaluated in full.
+/* gqa_prefill with a caller mask (arguments otherwise as gqa_prefill).  On a
+ * bf16 or fp16 plan of head size 64 or 128 without softcap, a boolean mask
+ * whose data and strides are multiples of 8 bytes, or an additive one whose
+ * data is 16-byte aligned and strides multiples of 4 elements, runs on the
+ * matrix-core prefill: each wave reads its rows' entries of a 64-key tile (a
+ * boolean mask one tile ahead, skipping a tile it clears for all 32 rows; an
+ * additive mask at the start of the tile, evaluated in full).  Other masks run
+ * on the streaming one-wavefront-per-row kernel, which skips a 64-key block
+ * with no key left (the all-false block skipping of "Attention Kernel
+ * Design", section "Compute paths").
  * Errors: as gqa_prefill, and INVALID_ARG for a NULL mask, an unknown kind or
  *   a negative stride, UNSUPPORTED for a misaligned additive mask. */
 gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk,

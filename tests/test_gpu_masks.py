@@ -37,14 +37,17 @@ def _block_sparse(seed, Lq, Lk, block=64):
     return torch.from_numpy(m[None, None])
 
 
-# Boolean masks with 8-byte-aligned rows (Lk % 8 == 0 here), bf16/f16, head
-# size 64 or 128 and no softcap run on the matrix-core prefill; the others on
-# the streaming kernel.  Both kinds of case are listed.
+# Boolean masks with 8-byte-aligned rows (Lk % 8 == 0 here) and additive ones
+# with 16-byte-aligned rows (Lk % 4 == 0), bf16/f16, head size 64 or 128 and no
+# softcap run on the matrix-core prefill; the others on the streaming kernel.
+# Both kinds of case are listed.
 PREFILL = [
     # (dtype, B, Hq, Hkv, D, Lq, Lk, window, softcap, sink, nonpad, mask kind, mask shape)
     ("bf16", 1, 8, 2, 128, 300, 320, -1, 0.0, False, None, "sparse", "11"),   # matrix core
     ("f16", 2, 4, 4, 64, 130, 264, 100, 0.0, True, (264, 100), "bool", "bh"),  # matrix core
     ("bf16", 2, 16, 2, 128, 96, 1000, 300, 0.0, False, None, "bool", "1h"),    # matrix core, Lq < Lk
+    ("bf16", 2, 8, 2, 128, 130, 256, 100, 0.0, True, None, "add", "1h"),      # matrix core
+    ("f16", 1, 4, 4, 64, 96, 268, -1, 0.0, False, (200,), "add", "bh"),       # matrix core, tail run
     ("bf16", 2, 8, 2, 128, 200, 200, 64, 0.0, True, (200, 150), "bool", "b1"),
     ("bf16", 2, 8, 2, 128, 130, 257, -1, 0.0, False, None, "add", "1h"),
     ("f16", 1, 4, 4, 64, 96, 96, -1, 30.0, True, None, "add", "bh"),
@@ -133,13 +136,18 @@ def test_all_true_mask_equals_the_unmasked_kernels(gpu):
     compare(b, want, "bf16", "no mask")
 
 
-def test_masked_prefill_full_size_sampled(gpu):
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_masked_prefill_full_size_sampled(gpu, kind):
     """The long prompt (32 heads x 8192 rows, window 4096) with a block-sparse
-    boolean mask, as the benchmark runs it; sampled rows against the oracle."""
+    mask (boolean, or additive 0 / -inf with noise on the kept keys), as the
+    benchmark runs it; sampled rows against the oracle."""
     from windowed_gqa_kv_amd.inputs import WORKLOADS
     w = WORKLOADS[3]
     d = generate(w)
     mask = _block_sparse(5, w.Lq, w.Lk)
+    if kind == "add":
+        noise = np.random.default_rng(6).standard_normal(mask.shape).astype(np.float32)
+        mask = torch.from_numpy(np.where(mask.numpy(), noise, -np.inf).astype(np.float32))
     plan = make_plan(w)
     out = plan.prefill(d["q"].cuda(), d["k"].cuda(), d["v"].cuda(), mask=mask.cuda())
     torch.cuda.synchronize()
@@ -150,5 +158,5 @@ def test_masked_prefill_full_size_sampled(gpu):
         g = h // G
         want = oracle.prefill(to_f64(d["q"][:, h:h + 1]), to_f64(d["k"][:, g:g + 1]),
                               to_f64(d["v"][:, g:g + 1]), scale=w.sm_scale, window=w.window,
-                              rows=rows, mask=mask.numpy())
+                              rows=rows, mask=mask.numpy() if kind == "bool" else mask.numpy().astype(np.float64))
         compare(out[:, h:h + 1, rows], want, "bf16", f"full-size masked head {h}")

@@ -57,11 +57,12 @@ struct AttnArgs {
   // Caller mask over [B, Hq, Lq, Lk] (element strides, 0 broadcasts, keys
   // contiguous; the key index is the position): kind 1 boolean (uint8,
   // nonzero attends), kind 2 additive fp32 (added to the scaled logit
-  // before softcap; -inf removes the key).  Only the generic kernel reads it.
+  // before softcap; -inf removes the key).
   const void* mask;
   int64_t m_sb, m_sh, m_sq;
   int32_t mask_kind;    // 0 = none
   float inv_cap;        // 1 / softcap (softcap > 0 only)
+  float bias_mul;       // 1 / scale: an additive mask value in raw score units
   float scale_log2;     // scale * log2(e)
   float scale_over_cap; // scale / softcap (softcap > 0 only)
   float cap_log2;       // softcap * log2(e)

@@ -450,14 +450,18 @@ GQA_API gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, in
   a.head_sink = head_sink;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int dtype = (int)plan->attrs.dtype;
-  // Boolean masks whose rows are 8-byte aligned run on the matrix-core kernel
-  // (it reads 8 mask bytes per aligned run of keys); anything else (additive
-  // masks, softcap, other layouts) on the streaming kernel.
+  // Masks whose runs of 8 keys are aligned (boolean: rows at multiples of 8
+  // bytes; additive: of 16 bytes) run on the matrix-core kernel; softcap and
+  // other layouts on the streaming kernel.
   const bool small_strides = a.k_ss < (int64_t(1) << 24) && a.v_ss < (int64_t(1) << 24);
-  const bool aligned8 = reinterpret_cast<uintptr_t>(mask->data) % 8 == 0 && mask->stride_b % 8 == 0 &&
-                        mask->stride_h % 8 == 0 && mask->stride_q % 8 == 0;
+  const bool boolean = mask->kind == GQA_MASK_BOOL;
+  const int64_t ealign = boolean ? 8 : 4;  // elements per aligned unit (8 or 16 bytes)
+  const bool aligned = reinterpret_cast<uintptr_t>(mask->data) % (boolean ? 8 : 16) == 0 &&
+                       mask->stride_b % ealign == 0 && mask->stride_h % ealign == 0 &&
+                       mask->stride_q % ealign == 0;
+  a.bias_mul = 1.0f / plan->scale;
   if (Lk > 0 && small_strides && gqa::prefill_mfma_supported(dtype, plan->attrs.head_size) &&
-      plan->attrs.softcap == 0.0f && mask->kind == GQA_MASK_BOOL && aligned8)
+      plan->attrs.softcap == 0.0f && aligned)
     return hip_status(gqa::launch_prefill_mfma(a, dtype, false, stream), "masked prefill launch");
   return hip_status(gqa::launch_attn_generic(a, dtype, stream), "masked prefill launch");
 }

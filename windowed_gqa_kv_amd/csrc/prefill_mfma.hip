@@ -197,9 +197,12 @@ __device__ __forceinline__ void wait_vm() {
 // wait on by count.
 typedef __attribute__((address_space(1))) const uint64_t global_u64;
 typedef __attribute__((address_space(1))) const unsigned char global_u8;
+typedef __attribute__((address_space(1))) const f32x4 global_f32x4;
+typedef __attribute__((address_space(1))) const float global_f32;
 
 // Two waves per SIMD (two workgroups per CU): the register budget is 256.
-// MASK = 1: a caller boolean mask (uint8, nonzero attends) over [B, Hq, Lq, Lk].
+// MASK = 1: a caller boolean mask (uint8, nonzero attends) over [B, Hq, Lq, Lk];
+// MASK = 2: a caller additive mask (fp32, added to the scaled logit).
 template <bool IS_BF16, int D, bool SOFTCAP, int MASK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     AttnArgs a, int nrb, int items, int per_xcd, int hw) {
@@ -344,6 +347,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
   uint64_t mk_cur[4] = {0, 0, 0, 0}, mk_nxt[4] = {0, 0, 0, 0};
+  // Additive mask: the same runs as fp32 (two aligned 16-byte loads each),
+  // loaded at the start of the tile that uses them: the K Q^T MFMAs cover the
+  // latency, and every tile is evaluated in full.  bias / scale in raw score
+  // units, so that the log2 scaling adds bias * log2(e).
+  global_f32* frow = nullptr;
+  if constexpr (MASK == 2)
+    frow = (global_f32*)(reinterpret_cast<const float*>(a.mask) + b * a.m_sb + h * a.m_sh +
+                         (int64_t)min(my_row, a.Lq - 1) * a.m_sq);
+  f32x4 bias[4][2];
+  auto bias_load = [&](int kb) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int s0 = kb + 16 * x + 8 * h2;
+      if (s0 + 8 <= a.Lk) {
+        bias[x][0] = *(global_f32x4*)(frow + s0);
+        bias[x][1] = *(global_f32x4*)(frow + s0 + 4);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bias[x][e >> 2][e & 3] = s0 + e < a.Lk ? frow[s0 + e] : 0.0f;
+      }
+    }
+  };
   const int kr0 = key_of_m(n);                        // this lane's K row in a sub-tile
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0];
@@ -442,6 +467,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int r2 = 0; r2 < 16; ++r2) {
           const uint64_t run = mk_cur[2 * sub + (r2 >> 3)];
           acc[r2] = ((run >> (8 * (r2 & 7))) & 0xffu) ? acc[r2] : -INFINITY;
+        }
+      }
+      if constexpr (MASK == 2) {  // -inf (or NaN) removes the key
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) {
+          const float bv = bias[2 * sub + (r2 >> 3)][(r2 >> 2) & 1][r2 & 3];
+          acc[r2] = bv > -INFINITY ? fmaf(bv, a.bias_mul, acc[r2]) : -INFINITY;
         }
       }
 #pragma unroll
@@ -560,6 +592,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       a0 = a0 && __any((mk_cur[0] | mk_cur[1]) != 0);
       a1 = a1 && __any((mk_cur[2] | mk_cur[3]) != 0);
     }
+    if constexpr (MASK == 2)
+      if (a0 || a1) bias_load(kb);
     if (a0 || a1) {
       qk(stage_tag, sc, dma_at);
       float alpha;
@@ -609,7 +643,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 template <bool IS_BF16, int D>
 hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
-  if (a.mask_kind != 0 && (softcap || a.mask_kind != 1)) return hipErrorInvalidValue;
+  if (a.mask_kind != 0 && softcap) return hipErrorInvalidValue;
   // heads per workgroup: the largest power of two that divides G, at most 8
   const int hw = std::min(a.G & -a.G, kWaves);
   const int rpw = 32 * (kWaves / hw);
@@ -619,6 +653,8 @@ hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
   dim3 grid(8 * per_xcd), block(64 * kWaves);
   if (a.mask_kind == 1)
     hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false, 1>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
+  else if (a.mask_kind == 2)
+    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false, 2>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
   else if (softcap)
     hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, true, 0>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
   else
