@@ -405,6 +405,34 @@ def bench_masks(steps):
                      "kernel_ms": round(ms, 4), "kept_pairs": pairs, "achieved": round(tf, 2),
                      "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
         del md
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    # the headline decode with a random boolean mask over [B, Hq, 1, capacity]
+    # (90% of the keys kept), against the same launches without a mask: eager
+    # launches, HIP events around each
+    wd = WORKLOADS[2]
+    d = generate(wd)
+    plan = binding.Plan(wd.Hq, wd.Hkv, wd.D, dtype=wd.dtype, smooth_softmax=wd.smooth_softmax,
+                        max_batch=wd.B, max_q_len=wd.Lq, max_kv_len=wd.Lk)
+    kc, vc = d["k_cache"].cuda(), d["v_cache"].cuda()
+    q, seq = d["q"].cuda(), d["seqlens_k"].cuda()
+    out = torch.empty_like(q)
+    ws = plan.new_workspace()
+    md = torch.from_numpy(np.random.default_rng(12).random((wd.B, wd.Hq, 1, wd.Lk)) < 0.9).cuda()
+    times = {}
+    for name, m in (("decode_unmasked", None), ("decode_bool_mask", md)):
+        for _ in range(5):
+            plan.decode(q, kc, vc, seq, out, workspace=ws, mask=m)
+        evs = _events(steps * 10)
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record()
+            plan.decode(q, kc, vc, seq, out, workspace=ws, mask=m)
+            b.record()
+        torch.cuda.synchronize()
+        times[name] = round(sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2] * 1e3, 2)
+    res["decode"] = {"workload": wd.name, "kernel": "decode_kernel", "median_us_per_eager_launch": times,
+                     "note": "warm cache (one replica); events around each eager launch"}
     return res
 
 

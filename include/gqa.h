@@ -264,13 +264,19 @@ gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk
                               const gqa_mask* mask, void* hip_stream);
 
 /* gqa_decode with a caller mask over [B, Hq, curr, capacity] (arguments
- * otherwise as gqa_decode; no workspace).  Same kernel and rules as
- * gqa_prefill_masked.  Errors: as gqa_decode and gqa_prefill_masked, and
- *   UNSUPPORTED with a rolling cache (positions pass the mask's width). */
+ * otherwise as gqa_decode).  With a workspace (as gqa_decode's), a bf16/fp16
+ * plan of head size 64, 128 or 256 without softcap, and a mask whose data and
+ * strides are multiples of 4 bytes (boolean) or 16 bytes and 4 elements
+ * (additive), it runs on the matrix-core split-KV decode, each lane reading
+ * its 4 entries of a 16-key unit one unit ahead.  Otherwise (or with a NULL
+ * workspace) it runs on the streaming kernel of gqa_prefill_masked.
+ * Errors: as gqa_decode and gqa_prefill_masked, and UNSUPPORTED with a
+ *   rolling cache (positions pass the mask's width). */
 gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
                              gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache,
                              gqa_tensor out, const int32_t* seqlens_k, const float* head_sink,
-                             const gqa_mask* mask, void* hip_stream);
+                             const gqa_mask* mask, void* workspace, size_t ws_bytes,
+                             void* hip_stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* gqa_last_error(void);

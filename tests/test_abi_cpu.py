@@ -210,8 +210,10 @@ def test_mask_validation():
     ok = B.gqa_mask(FAKE, 0, 0, 1024, B.GQA_MASK_BOOL)
     def pf(mask, Bn=2, **kw):
         return B.gqa_prefill_masked(h, Bn, 8, 8, t(), t(), t(), t(), None, None, mask, None)
-    def dc(mask, Bn=2, hh=h):
-        return B.gqa_decode_masked(hh, Bn, 1, 64, t(), t(), t(), t(), s, None, mask, None)
+    ws = B.gqa_workspace_size(h)
+    def dc(mask, Bn=2, hh=h, wsp=None, wsb=0):
+        return B.gqa_decode_masked(hh, Bn, 1, 64, t(), t(), t(), t(), s, None, mask,
+                                   ctypes.c_void_p(wsp) if wsp else None, wsb, None)
     assert pf(None) == B.GQA_ERR_INVALID_ARG and "mask" in B.gqa_last_error()
     assert pf(B.gqa_mask(0, 0, 0, 8, 1)) == B.GQA_ERR_INVALID_ARG and "mask.data" in B.gqa_last_error()
     assert pf(B.gqa_mask(FAKE, 0, 0, 8, 3)) == B.GQA_ERR_INVALID_ARG and "kind" in B.gqa_last_error()
@@ -221,6 +223,10 @@ def test_mask_validation():
     assert pf(ok, Bn=0) == B.GQA_OK
     assert dc(None) == B.GQA_ERR_INVALID_ARG
     assert dc(ok, Bn=0) == B.GQA_OK
+    # the matrix-core path checks its workspace like gqa_decode
+    ok4 = B.gqa_mask(FAKE, 0, 0, 1024, B.GQA_MASK_BOOL)
+    assert dc(ok4, wsp=FAKE, wsb=16) == B.GQA_ERR_INVALID_ARG and "workspace" in B.gqa_last_error()
+    assert dc(ok4, wsp=FAKE + 8, wsb=ws) == B.GQA_ERR_INVALID_ARG and "aligned" in B.gqa_last_error()
     hr = plan(rolling_cache=1, local_window_size=8)
     assert dc(ok, hh=hr) == B.GQA_ERR_UNSUPPORTED and "rolling" in B.gqa_last_error()
 

@@ -92,14 +92,23 @@ def test_masked_prefill_matches_oracle(gpu, case):
         assert not out[:, :, row].any(), "a row with every key masked must be zero"
 
 
-@pytest.mark.parametrize("dtype,D,curr,cap,kind", [("bf16", 128, 1, 1024, "bool"),
-                                                    ("bf16", 256, 4, 600, "add"),
-                                                    ("f32", 32, 2, 100, "bool")])
-def test_masked_decode_matches_oracle(gpu, dtype, D, curr, cap, kind):
+# Masks whose rows are 4-byte (boolean) / 16-byte (additive) aligned, bf16/f16
+# and no softcap run on the matrix-core decode; the others on the streaming
+# kernel.
+@pytest.mark.parametrize("dtype,D,curr,cap,kind,softcap", [
+    ("bf16", 128, 1, 1024, "bool", 0.0),   # matrix core
+    ("bf16", 256, 4, 600, "add", 0.0),     # matrix core
+    ("f16", 64, 2, 300, "bool", 0.0),      # matrix core, last unit past the capacity
+    ("bf16", 128, 3, 1500, "add", 0.0),    # matrix core, several pieces per tile
+    ("bf16", 256, 4, 600, "add", 50.0),    # streaming (softcap)
+    ("bf16", 128, 1, 1022, "bool", 0.0),   # streaming (rows not 4-byte aligned)
+    ("f32", 32, 2, 100, "bool", 0.0),      # streaming (fp32)
+])
+def test_masked_decode_matches_oracle(gpu, dtype, D, curr, cap, kind, softcap):
     B, Hq, Hkv = 3, 8, 2
     seq = [cap - 1, 17, cap // 2]
     w = Workload("maskdec", "decode", dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, Lq=curr, Lk=cap,
-                 window=-1 if D != 256 else 200, softcap=50.0 if D == 256 else 0.0,
+                 window=-1 if D != 256 else 200, softcap=softcap,
                  smooth_softmax=True, seqlens=("list", seq), seed=400 + D + curr)
     d = generate(w)
     shape = (B, Hq, curr, cap)
@@ -117,6 +126,30 @@ def test_masked_decode_matches_oracle(gpu, dtype, D, curr, cap, kind):
                          softcap=w.softcap, smooth_softmax=True,
                          mask=mask.numpy() if kind == "bool" else mask.numpy().astype(np.float64))
     compare(out, want, dtype, f"masked decode {dtype} D={D} curr={curr}")
+
+
+def test_masked_decode_full_size(gpu):
+    """The headline decode workload (8 x 32 heads, caches of 4096) with a
+    random boolean mask over [B, Hq, 1, 4096] on the matrix-core decode,
+    against the oracle, and an all-True mask against the unmasked kernel's
+    result within the attention tolerance of the oracle."""
+    from windowed_gqa_kv_amd.inputs import WORKLOADS
+    w = WORKLOADS[2]
+    d = generate(w)
+    plan = make_plan(w)
+    kc, vc = d["k_cache"].cuda(), d["v_cache"].cuda()
+    seq_d = d["seqlens_k"].cuda()
+    plan.append_kv(d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, seq_d)
+    mask = _bool_mask(12, (w.B, w.Hq, 1, w.Lk), 0.9)
+    out = plan.decode(d["q"].cuda(), kc, vc, seq_d, mask=mask.cuda())
+    torch.cuda.synchronize()
+    s = d["seqlens_k"].numpy().astype(np.int64)
+    top = int(s.max()) + 1
+    kc_o, vc_o = oracle.append_kv(to_f64(d["k_cache"][:, :, :top]), to_f64(d["v_cache"][:, :, :top]),
+                                  to_f64(d["k_new"]), to_f64(d["v_new"]), s)
+    want = oracle.decode(to_f64(d["q"]), kc_o, vc_o, s, scale=w.sm_scale, smooth_softmax=True,
+                         mask=mask.numpy()[..., :top])
+    compare(out, want, "bf16", "full-size masked decode")
 
 
 def test_all_true_mask_equals_the_unmasked_kernels(gpu):

@@ -113,7 +113,7 @@ def load():
     MK = ctypes.POINTER(gqa_mask)
     lib.gqa_prefill_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, MK, P]
     lib.gqa_prefill_masked.restype = ctypes.c_int
-    lib.gqa_decode_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, MK, P]
+    lib.gqa_decode_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, MK, P, S, P]
     lib.gqa_decode_masked.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
@@ -174,9 +174,10 @@ def gqa_prefill_masked(plan, B, Lq, Lk, q, k, v, out, nonpad_kv_seqlen, head_sin
 
 
 def gqa_decode_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, mask,
-                      stream) -> int:
+                      workspace, ws_bytes, stream) -> int:
     return load().gqa_decode_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
-                                    head_sink, None if mask is None else ctypes.byref(mask), stream)
+                                    head_sink, None if mask is None else ctypes.byref(mask),
+                                    workspace, ws_bytes, stream)
 
 
 def gqa_last_error() -> str:
@@ -334,10 +335,13 @@ class Plan:
             out = torch.empty_like(q)
         if mask is not None:
             B, _, curr, _ = q.shape
+            if workspace is None:
+                workspace = self.new_workspace(q.device)
             check(gqa_decode_masked(self._h, B, curr, k_cache.shape[2], tensor_view(q),
                                     tensor_view(k_cache), tensor_view(v_cache), tensor_view(out),
                                     _ptr(seqlens_k), _ptr(head_sink),
                                     self.mask_view(mask, B, curr, k_cache.shape[2]),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
             return out
         if workspace is None:

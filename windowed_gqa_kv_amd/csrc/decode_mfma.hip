@@ -186,7 +186,10 @@ struct Tile {
   int lo, hi;        // union key interval (empty when lo > hi)
   int rows_tile;     // query rows in this tile (<= 16)
 };
-__device__ __forceinline__ Tile make_tile(const AttnArgs& a, int rows, int nrt, int t) {
+// With a caller mask the union interval starts at a multiple of 16 keys (the
+// keys before a row's band are masked like any other excluded key), so that a
+// lane's four mask entries of a unit form one aligned load.
+__device__ __forceinline__ Tile make_tile(const AttnArgs& a, int rows, int nrt, int t, bool align16) {
   Tile x;
   x.bg = t / nrt;
   x.rt = t - x.bg * nrt;
@@ -197,6 +200,7 @@ __device__ __forceinline__ Tile make_tile(const AttnArgs& a, int rows, int nrt, 
   x.rows_tile = min(kRowsPerTile, rows - r_first);
   x.lo = row_lo(a, x.sp.q_off + r_first / a.G);
   x.hi = row_hi(a, x.sp.q_off + (r_first + x.rows_tile - 1) / a.G, x.sp.valid);
+  if (align16 && x.lo <= x.hi) x.lo &= ~(kSub - 1);
   return x;
 }
 __device__ __forceinline__ int units_of(const Tile& x) {
@@ -379,7 +383,9 @@ __device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt,
     merge_tile_q<IS_BF16, D, 8>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
 }
 
-template <bool IS_BF16, int D, bool SOFTCAP>
+// MASK = 1 / 2: a caller boolean (uint8) / additive (fp32) mask over
+// [B, Hq, curr, capacity], the key index being the cache slot.
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int nrt,
                                                      float* __restrict__ part, unsigned* __restrict__ counters) {
   using RG = Ring<D>;
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     Tile x{};
     int ut = 0;
     if (lane < T) {
-      x = make_tile(a, rows, nrt, lane);
+      x = make_tile(a, rows, nrt, lane, MASK != 0);
       ut = units_of(x);
     }
     const int incl = wave_incl_scan(ut, lane);
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     __syncthreads();
   } else {
     block_scan(pre, [&](int t) {
-      const Tile x = make_tile(a, rows, nrt, t);
+      const Tile x = make_tile(a, rows, nrt, t, MASK != 0);
       if (cached) tcache[t] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
       return units_of(x);
     });
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   // tiles nobody streams (no allowed key for any of their rows) output zeros
   for (int t = k; t < T; t += G) {
     if (pre[t + 1] != pre[t]) continue;
-    const Tile x = make_tile(a, rows, nrt, t);
+    const Tile x = make_tile(a, rows, nrt, t, MASK != 0);
     for (int idx = tid; idx < x.rows_tile * (D / 4); idx += 256) {
       const int row = kRowsPerTile * x.rt + idx / (D / 4);
       store_row4<IS_BF16, D>(a, x.b, x.g * a.G + row % a.G, row / a.G, 4 * (idx % (D / 4)), f32x4{});
@@ -603,7 +609,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       x.hi = c.w;
       x.rows_tile = min(kRowsPerTile, rows - kRowsPerTile * x.rt);
     } else {
-      x = make_tile(a, rows, nrt, t);
+      x = make_tile(a, rows, nrt, t, MASK != 0);
     }
     const int c_lo = x.lo + kSub * ua;
     const int c_hi = min(x.hi, x.lo + kSub * ub - 1);
@@ -690,10 +696,51 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     for (int db = 0; db < DB; ++db) o[db] = f32x4{};
     float m_run = -INFINITY, l_run = 0.0f;
 
+    // Caller mask: this lane's row (padding rows read the tile's first row)
+    // and, per unit, its keys kb + 4 q4 .. + 3 -- one aligned 4-byte (boolean)
+    // or 16-byte (additive) load, a unit ahead; entries past the capacity are
+    // read one by one.  The loads are younger than the unit's DMA, so the
+    // counted waits below only grow stronger.
+    uint32_t mb_cur = 0, mb_nxt = 0;
+    f32x4 mf_cur = f32x4{}, mf_nxt = f32x4{};
+    const char* mrow = nullptr;
+    if constexpr (MASK != 0) {
+      const int mr = kRowsPerTile * x.rt + (row_ok ? n : 0);
+      mrow = reinterpret_cast<const char*>(a.mask) +
+             (MASK == 1 ? 1 : 4) * (x.b * a.m_sb + (int64_t)(x.g * a.G + mr % a.G) * a.m_sh +
+                                    (int64_t)(mr / a.G) * a.m_sq);
+    }
+    auto mask_load = [&](int kb) {
+      const int k0 = kb + 4 * q4;
+      if constexpr (MASK == 1) {
+        if (k0 + 3 < a.Lk) {
+          mb_nxt = *(const __attribute__((address_space(1))) uint32_t*)(mrow + k0);
+        } else {
+          uint32_t v = 0;
+          for (int e = 0; e < 4; ++e)
+            if (k0 + e < a.Lk) v |= (uint32_t)(*(const __attribute__((address_space(1))) uint8_t*)(mrow + k0 + e)) << (8 * e);
+          mb_nxt = v;
+        }
+      } else if constexpr (MASK == 2) {
+        const auto* fp = (const __attribute__((address_space(1))) float*)mrow;
+        if (k0 + 3 < a.Lk) {
+          mf_nxt = *(const __attribute__((address_space(1))) f32x4*)(fp + k0);
+        } else {
+          for (int e = 0; e < 4; ++e) mf_nxt[e] = k0 + e < a.Lk ? fp[k0 + e] : 0.0f;
+        }
+      }
+    };
+    if constexpr (MASK != 0)
+      if (nw > 0) mask_load(c_lo + kSub * w);
+
     for (int j = 0; j < nw; ++j) {
       const int s = j % S;
       wait_units<2 * RG::kDmaPerUnit, S>(min(S - 1, nw - 1 - j));
       const int kb = c_lo + kSub * (w + 4 * j);
+      if constexpr (MASK == 1) mb_cur = mb_nxt;
+      if constexpr (MASK == 2) mf_cur = mf_nxt;
+      if constexpr (MASK != 0)
+        if (j + 1 < nw) mask_load(kb + 4 * kSub);
       const uint32_t st = ring_addr + s * 2 * RG::kUnitBytes;
       // S^T = K Q^T
       u32x4 kf[KQ];
@@ -714,6 +761,14 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
           const int j2 = kb + 4 * q4 + r;
           sc[r] = (j2 < lo_eff || j2 > hi_eff) ? -INFINITY : sc[r];
         }
+      }
+      if constexpr (MASK == 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = ((mb_cur >> (8 * r)) & 0xffu) ? sc[r] : -INFINITY;
+      }
+      if constexpr (MASK == 2) {  // -inf (or NaN) removes the key
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = mf_cur[r] > -INFINITY ? fmaf(mf_cur[r], a.bias_mul, sc[r]) : -INFINITY;
       }
       // online softmax: lanes n, n+16, n+32, n+48 share row n
       float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -855,9 +910,9 @@ int resident_grid(K kernel) {
   return std::max(1, std::min(kMaxGrid, cus * per_cu));
 }
 
-template <bool IS_BF16, int D, bool SOFTCAP>
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK>
 hipError_t launch_t(const AttnArgs& a, const DecodeGeometry& geo, float* ws, hipStream_t stream) {
-  auto kernel = decode_kernel<IS_BF16, D, SOFTCAP>;
+  auto kernel = decode_kernel<IS_BF16, D, SOFTCAP, MASK>;
   static int grid_cache[16] = {0};  // per device; a benign race computes the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
@@ -871,7 +926,12 @@ hipError_t launch_t(const AttnArgs& a, const DecodeGeometry& geo, float* ws, hip
 
 template <bool IS_BF16, int D>
 hipError_t launch_d(const AttnArgs& a, bool softcap, const DecodeGeometry& geo, float* ws, hipStream_t stream) {
-  return softcap ? launch_t<IS_BF16, D, true>(a, geo, ws, stream) : launch_t<IS_BF16, D, false>(a, geo, ws, stream);
+  if (a.mask_kind != 0) {  // masked launches carry no softcap (the host routes those elsewhere)
+    if (softcap) return hipErrorInvalidValue;
+    return a.mask_kind == 1 ? launch_t<IS_BF16, D, false, 1>(a, geo, ws, stream)
+                            : launch_t<IS_BF16, D, false, 2>(a, geo, ws, stream);
+  }
+  return softcap ? launch_t<IS_BF16, D, true, 0>(a, geo, ws, stream) : launch_t<IS_BF16, D, false, 0>(a, geo, ws, stream);
 }
 
 }  // namespace

@@ -469,7 +469,7 @@ GQA_API gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, in
 GQA_API gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
                                      gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
                                      const int32_t* seqlens_k, const float* head_sink, const gqa_mask* mask,
-                                     void* hip_stream) {
+                                     void* workspace, size_t ws_bytes, void* hip_stream) {
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -494,8 +494,26 @@ GQA_API gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, i
   if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
   a.seqlens = seqlens_k;
   a.head_sink = head_sink;
-  return hip_status(gqa::launch_attn_generic(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
-                    "masked decode launch");
+  a.bias_mul = 1.0f / plan->scale;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int dtype = (int)plan->attrs.dtype;
+  // The matrix-core decode reads a lane's 4 mask entries of a unit as one
+  // aligned load: boolean rows at multiples of 4 bytes, additive ones of 16.
+  const bool boolean = mask->kind == GQA_MASK_BOOL;
+  const bool aligned = reinterpret_cast<uintptr_t>(mask->data) % (boolean ? 4 : 16) == 0 &&
+                       mask->stride_b % 4 == 0 && mask->stride_h % 4 == 0 && mask->stride_q % 4 == 0;
+  if (workspace != nullptr && aligned && plan->attrs.softcap == 0.0f &&
+      gqa::decode_mfma_supported(dtype, plan->attrs.head_size)) {
+    gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
+    const size_t need = geo.ws_floats * sizeof(float);
+    if (ws_bytes < need) return fail(GQA_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (geo.fits)
+      return hip_status(gqa::launch_decode_mfma(a, dtype, false, geo, reinterpret_cast<float*>(workspace), stream),
+                        "masked decode launch");
+  }
+  return hip_status(gqa::launch_attn_generic(a, dtype, stream), "masked decode launch");
 }
 
 GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }
