@@ -10,6 +10,7 @@ nothing from the product path.
 ``brute``      the same definition with scalar Python loops, for tiny shapes.
 ``rotary``     rotary position embedding of Q and of K before it enters the cache.
 ``rolling``    the rolling (ring-buffer) KV cache of a windowed layer.
+``fp8``        an FP8 (E4M3) KV cache with per-tensor scales.
 """
 
 from .materialized import (  # noqa: F401
@@ -24,3 +25,4 @@ from .materialized import (  # noqa: F401
 from . import brute  # noqa: F401
 from . import rotary  # noqa: F401
 from . import rolling  # noqa: F401
+from . import fp8  # noqa: F401
