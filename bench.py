@@ -25,7 +25,8 @@ rotary embedding of the long prompt's Q and K (GB/s against HBM) and a decode
 step's append with rotary beside the plain append; `rolling` times the
 speculative-decode workload against a rolling cache of W + curr - 1 slots;
 `masks` times the long prompt through the masked (streaming) kernel with an
-all-True and a block-sparse boolean mask.
+all-True and a block-sparse boolean mask; `fp8` times the headline decode on
+FP8 (E4M3) caches.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
        [--no-cpu-baseline] [--workload NAME]
@@ -436,6 +437,52 @@ def bench_masks(steps):
     return res
 
 
+def bench_fp8(reps):
+    """The headline decode on FP8 (E4M3) caches (gqa_decode_fp8): graphs of
+    back-to-back decodes over 16 cache replicas (1 GiB), HIP events around the
+    replays.  Bytes: the K/V rows at one byte per element, Q and O."""
+    import torch
+    from windowed_gqa_kv_amd import binding, work
+    from windowed_gqa_kv_amd.inputs import WORKLOADS, generate
+
+    w = WORKLOADS[2]
+    d = generate(w)
+    ks = vs = 0.03
+    plan = binding.Plan(w.Hq, w.Hkv, w.D, dtype=w.dtype, smooth_softmax=w.smooth_softmax,
+                        max_batch=w.B, max_q_len=w.Lq, max_kv_len=w.Lk)
+    kc0 = (d["k_cache"].float() / ks).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+    vc0 = (d["v_cache"].float() / vs).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+    R = 16
+    caches = [(kc0.clone(), vc0.clone()) for _ in range(R)]
+    del kc0, vc0
+    q, seq = d["q"].cuda(), d["seqlens_k"].cuda()
+    kn, vn = d["k_new"].cuda(), d["v_new"].cuda()
+    out = torch.empty_like(q)
+    ws = plan.new_workspace()
+    for kc, vc in caches:
+        plan.append_kv_fp8(kn, vn, kc, vc, seq, ks, vs)
+        plan.decode_fp8(q, kc, vc, seq, ks, vs, out, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for kc, vc in caches:
+            plan.decode_fp8(q, kc, vc, seq, ks, vs, out, workspace=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = _events(reps)
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / (reps * R)
+    s = d["seqlens_k"].numpy().astype("int64")
+    b = work.decode_bytes(s, w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window, kv_dtype="fp8")
+    return {"workload": w.name, "kernel": "decode_kernel (FP8 caches)", "kernel_ms": round(ms, 5),
+            "bytes_per_launch": b, "achieved": round(b / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
+            "frac": round(b / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(w, d, budget_s=12.0):
     """The float64 oracle on full decode steps of the same workload, repeated
     until ~budget_s of CPU time; reported in the same unit (GB/s)."""
@@ -551,6 +598,7 @@ def main():
         line["rotary"] = bench_rotary(args.extra_steps, 3)
         line["rolling"] = bench_rolling(5)
         line["masks"] = bench_masks(3)
+        line["fp8"] = bench_fp8(5)
 
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, r["inputs"])
     print(json.dumps(line), flush=True)

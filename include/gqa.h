@@ -278,6 +278,37 @@ gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t c
                              const gqa_mask* mask, void* workspace, size_t ws_bytes,
                              void* hip_stream);
 
+/* FP8 (E4M3) KV cache (the pages name quantized KV caches only as outside
+ * their scope: "[NPUW] Support GQA sliding-window ...", section
+ * "smooth_softmax / head_sink"; every rule here is this library's reading).
+ * The caches are uint8 [B, Hkv, capacity, D] of OCP E4M3 codes (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; largest finite 448; no
+ * infinities), with one fp32 scale for K and one for V: K = decode(code) *
+ * k_scale.  Strides of the caches are in bytes (= elements), multiples of 16.
+ *
+ * gqa_append_kv_fp8: gqa_append_kv that quantizes the new rows (the plan's
+ * dtype): code = nearest E4M3 value of x * fp32(1 / scale) computed in fp32,
+ * ties to even, magnitudes beyond 448 saturated to 448, NaN to 0x7F.
+ * Errors: as gqa_append_kv, and INVALID_ARG for a scale that is not finite
+ * and positive. */
+gqa_status gqa_append_kv_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                             gqa_tensor k_new, gqa_tensor v_new,
+                             gqa_tensor k_cache, gqa_tensor v_cache,
+                             const int32_t* seqlens_k, float k_scale, float v_scale,
+                             void* hip_stream);
+
+/* gqa_decode against FP8 caches (arguments otherwise as gqa_decode).  The
+ * matrix-core split-KV decode streams the codes (half the bytes of a 16-bit
+ * cache), turns each 16-key unit into the plan's 16-bit type in LDS (exact),
+ * folds k_scale into the softmax scale and v_scale into the normalization.
+ * Needs a bf16 or fp16 plan of head size 64, 128 or 256 (UNSUPPORTED
+ * otherwise).  Errors: as gqa_decode, and INVALID_ARG for a bad scale. */
+gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                          gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                          const int32_t* seqlens_k, const float* head_sink,
+                          float k_scale, float v_scale,
+                          void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* gqa_last_error(void);
 

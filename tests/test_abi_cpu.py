@@ -23,7 +23,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-NULL address; never dereferenced
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", src)))
 
 
 def attrs(**kw):
@@ -229,6 +229,30 @@ def test_mask_validation():
     assert dc(ok4, wsp=FAKE + 8, wsb=ws) == B.GQA_ERR_INVALID_ARG and "aligned" in B.gqa_last_error()
     hr = plan(rolling_cache=1, local_window_size=8)
     assert dc(ok, hh=hr) == B.GQA_ERR_UNSUPPORTED and "rolling" in B.gqa_last_error()
+
+
+def test_fp8_validation():
+    h = plan()
+    s = ctypes.c_void_p(FAKE)
+    ws = B.gqa_workspace_size(h)
+    c8 = B.gqa_tensor(FAKE, 1024 * 128 * 2, 1024 * 128, 128)  # byte strides of a uint8 cache
+    def app(ks=1.0, vs=1.0, kc=c8, Bn=2):
+        return B.gqa_append_kv_fp8(h, Bn, 1, 64, t(), t(), kc, c8, s, ks, vs, None)
+    def dec(ks=1.0, vs=1.0, hh=h, wsp=FAKE, kc=c8, Bn=2):
+        return B.gqa_decode_fp8(hh, Bn, 1, 64, t(), kc, c8, t(), s, None, ks, vs,
+                                ctypes.c_void_p(wsp) if wsp else None, ws, None)
+    assert app(ks=0.0) == B.GQA_ERR_INVALID_ARG and "scale" in B.gqa_last_error()
+    assert app(vs=float("inf")) == B.GQA_ERR_INVALID_ARG
+    assert app(kc=B.gqa_tensor(FAKE, 1024 * 128 * 2, 1024 * 128, 100)) == B.GQA_ERR_UNSUPPORTED
+    assert app(Bn=0) == B.GQA_OK
+    assert dec(ks=-1.0) == B.GQA_ERR_INVALID_ARG
+    assert dec(wsp=0) == B.GQA_ERR_INVALID_ARG and "workspace" in B.gqa_last_error()
+    assert dec(Bn=0) == B.GQA_OK
+    st, h96 = B.gqa_plan(attrs(head_size=96), 4, 16, 1024)
+    assert st == B.GQA_OK
+    assert dec(hh=h96) == B.GQA_ERR_UNSUPPORTED and "FP8" in B.gqa_last_error()
+    st, hf = B.gqa_plan(attrs(dtype=B.GQA_F32), 4, 16, 1024)
+    assert dec(hh=hf) == B.GQA_ERR_UNSUPPORTED
 
 
 def test_last_error_is_thread_local_and_specific():

@@ -32,7 +32,8 @@ DTYPE_CODES = {"f32": GQA_F32, "f16": GQA_F16, "bf16": GQA_BF16}
 
 EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
-            "gqa_prefill_masked", "gqa_decode_masked", "gqa_last_error")
+            "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
+            "gqa_last_error")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
@@ -115,6 +116,11 @@ def load():
     lib.gqa_prefill_masked.restype = ctypes.c_int
     lib.gqa_decode_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, MK, P, S, P]
     lib.gqa_decode_masked.restype = ctypes.c_int
+    F = ctypes.c_float
+    lib.gqa_append_kv_fp8.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, F, F, P]
+    lib.gqa_append_kv_fp8.restype = ctypes.c_int
+    lib.gqa_decode_fp8.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, F, F, P, S, P]
+    lib.gqa_decode_fp8.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -178,6 +184,18 @@ def gqa_decode_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens
     return load().gqa_decode_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
                                     head_sink, None if mask is None else ctypes.byref(mask),
                                     workspace, ws_bytes, stream)
+
+
+def gqa_append_kv_fp8(plan, B, curr, capacity, k_new, v_new, k_cache, v_cache, seqlens_k, k_scale,
+                      v_scale, stream) -> int:
+    return load().gqa_append_kv_fp8(plan, B, curr, capacity, k_new, v_new, k_cache, v_cache,
+                                    seqlens_k, k_scale, v_scale, stream)
+
+
+def gqa_decode_fp8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scale,
+                   v_scale, workspace, ws_bytes, stream) -> int:
+    return load().gqa_decode_fp8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
+                                 head_sink, k_scale, v_scale, workspace, ws_bytes, stream)
 
 
 def gqa_last_error() -> str:
@@ -391,3 +409,31 @@ class Plan:
                                    tensor_view(k_cache), tensor_view(v_cache), _ptr(seqlens_k),
                                    self._tables(cos, sin), _stream(stream)))
         return q_rot
+
+    # ---- FP8 (E4M3) KV caches: uint8 tensors of codes, per-tensor scales ----
+    def append_kv_fp8(self, k_new, v_new, k_cache, v_cache, seqlens_k, k_scale, v_scale, *, stream=None):
+        import torch
+        self._check_dtype(k_new, v_new)
+        if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+            raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+        B, _, curr, _ = k_new.shape
+        check(gqa_append_kv_fp8(self._h, B, curr, k_cache.shape[2], tensor_view(k_new),
+                                tensor_view(v_new), tensor_view(k_cache), tensor_view(v_cache),
+                                _ptr(seqlens_k), float(k_scale), float(v_scale), _stream(stream)))
+
+    def decode_fp8(self, q, k_cache, v_cache, seqlens_k, k_scale, v_scale, out=None, *,
+                   head_sink=None, workspace=None, stream=None):
+        import torch
+        self._check_dtype(q)
+        if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+            raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.new_workspace(q.device)
+        B, _, curr, _ = q.shape
+        check(gqa_decode_fp8(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_cache),
+                             tensor_view(v_cache), tensor_view(out), _ptr(seqlens_k), _ptr(head_sink),
+                             float(k_scale), float(v_scale), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+        return out

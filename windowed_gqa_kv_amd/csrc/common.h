@@ -63,6 +63,11 @@ struct AttnArgs {
   int32_t mask_kind;    // 0 = none
   float inv_cap;        // 1 / softcap (softcap > 0 only)
   float bias_mul;       // 1 / scale: an additive mask value in raw score units
+  // Decode on FP8 (E4M3) caches: k and v hold codes (byte strides), the K
+  // scale is folded into scale_log2 / scale_over_cap, the V scale multiplies
+  // the normalized output.
+  int32_t kv_fp8;
+  float v_scale;        // 1 unless kv_fp8
   float scale_log2;     // scale * log2(e)
   float scale_over_cap; // scale / softcap (softcap > 0 only)
   float cap_log2;       // softcap * log2(e)

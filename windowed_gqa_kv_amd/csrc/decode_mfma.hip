@@ -41,6 +41,7 @@
 // 16-byte chunks (chosen per lane in the DMA source address) so that both
 // LDS read patterns are free of bank conflicts.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -60,15 +61,23 @@ constexpr int kNonTemporal = 2;       // cache-policy bits of a load: nt (gfx950
 // wave for head sizes up to 128 (two workgroups share a CU, so one wave's
 // softmax overlaps another's loads) and 32 KB at head size 256 (two stages of
 // 16 KB units; one workgroup per CU).
-template <int D>
+// An FP8 (E4M3) cache (KV8) streams units of D bytes per key row into kStages
+// row-major fp8 stages and converts the unit about to be computed into one
+// 16-bit K + V buffer of the usual layout; the footprint is unchanged.
+template <int D, bool KV8 = false>
 struct Ring {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kSlots = D / 8;                     // 16-byte chunks per key row
-  static constexpr int kUnitBytes = kSub * kRowBytes;      // K (or V) bytes of one unit
-  static constexpr int kDmaPerUnit = kUnitBytes / 1024;    // wave-wide 16-byte DMA loads
-  static constexpr int kStages = (D >= 256 ? 32768 : 16384) / (2 * kUnitBytes);
-  static constexpr int kWaveBytes = kStages * 2 * kUnitBytes;
-  static_assert(kUnitBytes % 1024 == 0, "a unit is whole DMA instructions");
+  static constexpr int kUnitBytes = kSub * kRowBytes;      // K (or V) bytes of one 16-bit unit
+  static constexpr int kInBytes = KV8 ? kSub * D : kUnitBytes;  // K (or V) bytes of one streamed unit
+  static constexpr int kDmaPerUnit = kInBytes / 1024;      // wave-wide 16-byte DMA loads
+  static constexpr int kBudget = D >= 256 ? 32768 : 16384;
+  static constexpr int kBufBytes = KV8 ? 2 * kUnitBytes : 0;
+  static constexpr int kStages = (kBudget - kBufBytes) / (2 * kInBytes);
+  static constexpr int kBufOff = kStages * 2 * kInBytes;  // the converted K + V unit (KV8)
+  static constexpr int kWaveBytes = kBufOff + kBufBytes;
+  static_assert(kInBytes % 1024 == 0, "a unit is whole DMA instructions");
+  static_assert(kStages >= 2, "at least two units in flight");
   static_assert((kStages - 1) * 2 * kDmaPerUnit <= 63, "vmcnt range");
 };
 
@@ -353,6 +362,7 @@ __device__ __forceinline__ void merge_tile_q(const AttnArgs& a, int lrp, int R, 
       } else {
         fac = 1.0f / Ls;
       }
+      fac *= a.v_scale;  // an FP8 V cache holds V / v_scale (1 otherwise)
 #pragma unroll
       for (int q = 0; q < QPL; ++q) store_row4<IS_BF16, D>(a, xb, h, row / a.G, 4 * (c * QPL + q), acc[q] * fac);
     }
@@ -385,10 +395,11 @@ __device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt,
 
 // MASK = 1 / 2: a caller boolean (uint8) / additive (fp32) mask over
 // [B, Hq, curr, capacity], the key index being the cache slot.
-template <bool IS_BF16, int D, bool SOFTCAP, int MASK>
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int nrt,
                                                      float* __restrict__ part, unsigned* __restrict__ counters) {
-  using RG = Ring<D>;
+  using RG = Ring<D, KV8>;
+  using KT = std::conditional_t<KV8, uint8_t, uint16_t>;  // cache element
   constexpr int KQ = D / 32;    // k-steps of 16x16x32 over the head dim
   constexpr int DB = D / 16;    // 16-wide output blocks
   constexpr int S = RG::kStages;
@@ -624,8 +635,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     const int p_first = x.sp.q_off + (kRowsPerTile * x.rt) / a.G;
     const int p_last = x.sp.q_off + (kRowsPerTile * x.rt + x.rows_tile - 1) / a.G;
 
-    const uint16_t* __restrict__ Kg = reinterpret_cast<const uint16_t*>(a.k) + x.b * a.k_sb + x.g * a.k_sh;
-    const uint16_t* __restrict__ Vg = reinterpret_cast<const uint16_t*>(a.v) + x.b * a.v_sb + x.g * a.v_sh;
+    const KT* __restrict__ Kg = reinterpret_cast<const KT*>(a.k) + x.b * a.k_sb + x.g * a.k_sh;
+    const KT* __restrict__ Vg = reinterpret_cast<const KT*>(a.v) + x.b * a.v_sb + x.g * a.v_sh;
 
     // Q tile -> LDS by DMA, shared by the 4 waves (instruction i by wave i % 4).
     // Padding rows load the tile's last real row (in bounds, finite); MFMA
@@ -655,22 +666,25 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     // finite, masked out for every query row): no per-lane branches.
     auto issue_t = [&](int s, int j, auto ring_tag) {
       const int kb = c_lo + kSub * (w + 4 * j);
-      unsigned char* kdst = my_ring + s * 2 * RG::kUnitBytes;
-      unsigned char* vdst = kdst + RG::kUnitBytes;
+      unsigned char* kdst = my_ring + s * 2 * RG::kInBytes;
+      unsigned char* vdst = kdst + RG::kInBytes;
 #pragma unroll
       for (int i = 0; i < RG::kDmaPerUnit; ++i) {
         const int pos = 64 * i + lane;                 // 16-byte chunk position in the unit
-        const int key = pos / RG::kSlots;
-        const int cc = (pos % RG::kSlots) ^ swz<D>(key);  // the global chunk stored there
+        // 16-bit caches: swizzled chunks (global chunk cc of key row `key`);
+        // fp8 caches: row-major (byte offset 16 pos = key * D + 16 cc)
+        const int key = KV8 ? pos / (D / 16) : pos / RG::kSlots;
+        const int cc = KV8 ? pos % (D / 16) : (pos % RG::kSlots) ^ swz<D>(key);
         int row = min(kb + key, c_hi);
         if constexpr (decltype(ring_tag)::value) {
           row -= turns;
           row = row >= a.ring ? row - a.ring : row;
         }
         // K/V bytes are read once per call: non-temporal (streaming) loads
-        __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)row * a.k_ss + 8 * cc),
+        constexpr int kEl = KV8 ? 16 : 8;  // elements per 16-byte chunk
+        __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)row * a.k_ss + kEl * cc),
                                          (lds_void*)(kdst + 1024 * i), 16, 0, kNonTemporal);
-        __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)row * a.v_ss + 8 * cc),
+        __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)row * a.v_ss + kEl * cc),
                                          (lds_void*)(vdst + 1024 * i), 16, 0, kNonTemporal);
       }
     };
@@ -741,7 +755,38 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       if constexpr (MASK == 2) mf_cur = mf_nxt;
       if constexpr (MASK != 0)
         if (j + 1 < nw) mask_load(kb + 4 * kSub);
-      const uint32_t st = ring_addr + s * 2 * RG::kUnitBytes;
+      if constexpr (KV8) {
+        // fp8 stage -> the 16-bit K + V buffer, in the layout of the 16-bit
+        // path (bf16 / fp16 chunk g of key row r at slot g ^ swz(r)); every
+        // E4M3 value is exact in both types.  The stage is then refilled.
+        const unsigned char* s8 = my_ring + s * 2 * RG::kInBytes;
+        unsigned char* bb = my_ring + RG::kBufOff;
+#pragma unroll
+        for (int tsr = 0; tsr < 2; ++tsr)
+#pragma unroll
+          for (int i = 0; i < RG::kDmaPerUnit; ++i) {
+            const int pos = 64 * i + lane;
+            const int key = pos / (D / 16), c = pos % (D / 16);
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(s8 + tsr * RG::kInBytes + 16 * pos);
+            uint32_t hw[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[q], false);
+              const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[q], true);
+              hw[2 * q] = pack2<IS_BF16>(p0[0], p0[1]);
+              hw[2 * q + 1] = pack2<IS_BF16>(p1[0], p1[1]);
+            }
+            unsigned char* rowp = bb + tsr * RG::kUnitBytes + key * RG::kRowBytes;
+            *reinterpret_cast<u32x4*>(rowp + 16 * ((2 * c) ^ swz<D>(key))) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+            *reinterpret_cast<u32x4*>(rowp + 16 * ((2 * c + 1) ^ swz<D>(key))) = u32x4{hw[4], hw[5], hw[6], hw[7]};
+          }
+        // the operand reads below are inline assembly that counts its own LDS
+        // operations: the buffer writes (and the stage reads) must be done
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        if (j + S < nw) issue(s, j + S);
+      }
+      const uint32_t st = KV8 ? ring_addr + RG::kBufOff : ring_addr + s * 2 * RG::kUnitBytes;
       // S^T = K Q^T
       u32x4 kf[KQ];
 #pragma unroll
@@ -802,7 +847,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = mma_pv<IS_BF16>(vf[db], pp, o[db]);
       // refill this stage (its LDS reads are consumed above)
-      if (j + S < nw) issue(s, j + S);
+      if constexpr (!KV8)
+        if (j + S < nw) issue(s, j + S);
     }
 
     // ---- merge the 4 waves through LDS (lane-to-lane: identical layouts) ----
@@ -910,9 +956,9 @@ int resident_grid(K kernel) {
   return std::max(1, std::min(kMaxGrid, cus * per_cu));
 }
 
-template <bool IS_BF16, int D, bool SOFTCAP, int MASK>
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8 = false>
 hipError_t launch_t(const AttnArgs& a, const DecodeGeometry& geo, float* ws, hipStream_t stream) {
-  auto kernel = decode_kernel<IS_BF16, D, SOFTCAP, MASK>;
+  auto kernel = decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8>;
   static int grid_cache[16] = {0};  // per device; a benign race computes the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
@@ -926,6 +972,11 @@ hipError_t launch_t(const AttnArgs& a, const DecodeGeometry& geo, float* ws, hip
 
 template <bool IS_BF16, int D>
 hipError_t launch_d(const AttnArgs& a, bool softcap, const DecodeGeometry& geo, float* ws, hipStream_t stream) {
+  if (a.kv_fp8) {  // FP8 caches: no caller mask
+    if (a.mask_kind != 0) return hipErrorInvalidValue;
+    return softcap ? launch_t<IS_BF16, D, true, 0, true>(a, geo, ws, stream)
+                   : launch_t<IS_BF16, D, false, 0, true>(a, geo, ws, stream);
+  }
   if (a.mask_kind != 0) {  // masked launches carry no softcap (the host routes those elsewhere)
     if (softcap) return hipErrorInvalidValue;
     return a.mask_kind == 1 ? launch_t<IS_BF16, D, false, 1>(a, geo, ws, stream)

@@ -93,6 +93,7 @@ gqa::AttnArgs make_args(const gqa_plan_s* p, const gqa_tensor& q, const gqa_tens
   a.scale_over_cap = p->attrs.softcap > 0 ? p->scale / p->attrs.softcap : 0.0f;
   a.cap_log2 = p->attrs.softcap > 0 ? p->attrs.softcap * log2e : 0.0f;
   a.inv_cap = p->attrs.softcap > 0 ? 1.0f / p->attrs.softcap : 0.0f;
+  a.v_scale = 1.0f;
   return a;
 }
 
@@ -514,6 +515,115 @@ GQA_API gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, i
                         "masked decode launch");
   }
   return hip_status(gqa::launch_attn_generic(a, dtype, stream), "masked decode launch");
+}
+
+namespace {
+
+gqa_status check_scales(float k_scale, float v_scale) {
+  if (!(k_scale > 0.0f) || !std::isfinite(k_scale) || !(v_scale > 0.0f) || !std::isfinite(v_scale))
+    return fail(GQA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  return GQA_OK;
+}
+
+// The FP8 cache path exists for the matrix-core decode's types and head sizes.
+gqa_status check_fp8_plan(const gqa_plan_s* p) {
+  const int dtype = (int)p->attrs.dtype;
+  if (!gqa::decode_mfma_supported(dtype, p->attrs.head_size))
+    return fail(GQA_ERR_UNSUPPORTED, "FP8 caches need a bf16 or fp16 plan of head size 64, 128 or 256");
+  return GQA_OK;
+}
+
+}  // namespace
+
+GQA_API gqa_status gqa_append_kv_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                     gqa_tensor k_new, gqa_tensor v_new, gqa_tensor k_cache,
+                                     gqa_tensor v_cache, const int32_t* seqlens_k, float k_scale,
+                                     float v_scale, void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (curr > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the plan's max_q_len %d", curr, plan->max_q_len);
+  if (capacity > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
+                (long long)plan->max_kv_len);
+  if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  gqa_status st = check_scales(k_scale, v_scale);
+  if (st != GQA_OK) return st;
+  if ((st = check_ring(plan, curr, capacity)) != GQA_OK) return st;
+  if (B == 0 || curr == 0) return GQA_OK;
+  if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("k_new", k_new, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("v_new", v_new, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, 1)) != GQA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, 1)) != GQA_OK) return st;
+  gqa::AppendArgs a{};
+  a.k_new = k_new.data;
+  a.v_new = v_new.data;
+  a.k_cache = k_cache.data;
+  a.v_cache = v_cache.data;
+  a.kn_sb = k_new.stride_b * esz; a.kn_sh = k_new.stride_h * esz; a.kn_ss = k_new.stride_s * esz;
+  a.vn_sb = v_new.stride_b * esz; a.vn_sh = v_new.stride_h * esz; a.vn_ss = v_new.stride_s * esz;
+  a.kc_sb = k_cache.stride_b; a.kc_sh = k_cache.stride_h; a.kc_ss = k_cache.stride_s;
+  a.vc_sb = v_cache.stride_b; a.vc_sh = v_cache.stride_h; a.vc_ss = v_cache.stride_s;
+  a.seqlens = seqlens_k;
+  a.B = B;
+  a.Hkv = plan->attrs.kv_num_heads;
+  a.curr = curr;
+  a.row_bytes = plan->attrs.head_size * esz;
+  a.capacity = (int32_t)capacity;
+  a.rolling = plan->attrs.rolling_cache;
+  a.k_rcp = 1.0f / k_scale;
+  a.v_rcp = 1.0f / v_scale;
+  return hip_status(gqa::launch_append_kv_fp8(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
+                    "append_kv_fp8 launch");
+}
+
+GQA_API gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                                  gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                  const int32_t* seqlens_k, const float* head_sink, float k_scale,
+                                  float v_scale, void* workspace, size_t ws_bytes, void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (curr > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the plan's max_q_len %d", curr, plan->max_q_len);
+  if (capacity > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
+                (long long)plan->max_kv_len);
+  if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  gqa_status st = check_fp8_plan(plan);
+  if (st != GQA_OK) return st;
+  if ((st = check_scales(k_scale, v_scale)) != GQA_OK) return st;
+  if ((st = check_sink(plan, head_sink)) != GQA_OK) return st;
+  if ((st = check_ring(plan, curr, capacity)) != GQA_OK) return st;
+  if (B == 0 || curr == 0) return GQA_OK;
+  if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("q", q, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, 1)) != GQA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, 1)) != GQA_OK) return st;
+  if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
+  gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
+  a.seqlens = seqlens_k;
+  a.head_sink = head_sink;
+  a.kv_fp8 = 1;
+  a.scale_log2 *= k_scale;      // scores of the codes times k_scale
+  a.scale_over_cap *= k_scale;
+  a.v_scale = v_scale;
+  gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
+  const size_t need = geo.ws_floats * sizeof(float);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(GQA_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
+                workspace ? "" : ", NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (!geo.fits)
+    return fail(GQA_ERR_UNSUPPORTED, "FP8 caches: at most %d row tiles per call", 2048);
+  return hip_status(gqa::launch_decode_mfma(a, (int)plan->attrs.dtype, plan->attrs.softcap > 0, geo,
+                                            reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(hip_stream)),
+                    "decode_fp8 launch");
 }
 
 GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
 
 
 def intervals(q_abs, valid, causal: bool, window: int):
@@ -68,11 +68,13 @@ def decode_union_keys(seqlens_k, curr, causal, window):
     return np.array(out, dtype=np.int64)
 
 
-def decode_bytes(seqlens_k, curr, Hq, Hkv, D, dtype, causal, window) -> int:
+def decode_bytes(seqlens_k, curr, Hq, Hkv, D, dtype, causal, window, kv_dtype=None) -> int:
+    """``kv_dtype`` ("fp8" for an FP8 cache) sizes the K/V rows when it
+    differs from the type of Q and O."""
     e = ELEM_BYTES[dtype]
     keys = int(decode_union_keys(seqlens_k, curr, causal, window).sum())
     B = len(np.asarray(seqlens_k).reshape(-1))
-    kv = 2 * keys * Hkv * D * e
+    kv = 2 * keys * Hkv * D * ELEM_BYTES[kv_dtype or dtype]
     qo = 2 * B * Hq * curr * D * e
     return kv + qo
 
