@@ -768,21 +768,24 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
             const int pos = 64 * i + lane;
             const int key = pos / (D / 16), c = pos % (D / 16);
             const u32x4 raw = *reinterpret_cast<const u32x4*>(s8 + tsr * RG::kInBytes + 16 * pos);
-            uint32_t hw[8];
+            uint32_t hw[8];  // two 16-bit values per word, byte order kept
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[q], false);
-              const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[q], true);
-              hw[2 * q] = pack2<IS_BF16>(p0[0], p0[1]);
-              hw[2 * q + 1] = pack2<IS_BF16>(p1[0], p1[1]);
+              if constexpr (IS_BF16) {
+                hw[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, false));
+                hw[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, true));
+              } else {
+                hw[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[q], 1.0f, false));
+                hw[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[q], 1.0f, true));
+              }
             }
             unsigned char* rowp = bb + tsr * RG::kUnitBytes + key * RG::kRowBytes;
             *reinterpret_cast<u32x4*>(rowp + 16 * ((2 * c) ^ swz<D>(key))) = u32x4{hw[0], hw[1], hw[2], hw[3]};
             *reinterpret_cast<u32x4*>(rowp + 16 * ((2 * c + 1) ^ swz<D>(key))) = u32x4{hw[4], hw[5], hw[6], hw[7]};
           }
-        // the operand reads below are inline assembly that counts its own LDS
-        // operations: the buffer writes (and the stage reads) must be done
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        // A wave's LDS operations complete in order, so the counted waits of
+        // the operand reads below also cover these writes; the stage's reads
+        // have returned (their values are converted above) before the refill.
         asm volatile("" ::: "memory");
         if (j + S < nw) issue(s, j + S);
       }
