@@ -365,8 +365,9 @@ def bench_masks(steps):
     all-True mask (every pair of the band evaluated) and a block-sparse one
     (about half of the 64-key blocks of every 16-row group cleared; a wave
     skips a tile its 32 rows all lose); and the same block-sparse mask as an
-    additive 0 / -inf mask, evaluated in full.  FLOPs are 4*D per kept pair
-    of band and mask."""
+    additive 0 / -inf mask, evaluated in full; and the block-sparse boolean
+    mask again with a softcap of 50 on the logits.  FLOPs are 4*D per kept
+    pair of band and mask."""
     import numpy as np
     import torch
     from windowed_gqa_kv_amd import binding
@@ -376,6 +377,8 @@ def bench_masks(steps):
     d = generate(w)
     plan = binding.Plan(w.Hq, w.Hkv, w.D, dtype=w.dtype, local_window_size=w.window,
                         max_batch=w.B, max_q_len=w.Lq, max_kv_len=w.Lk)
+    capped = binding.Plan(w.Hq, w.Hkv, w.D, dtype=w.dtype, local_window_size=w.window, softcap=50.0,
+                          max_batch=w.B, max_q_len=w.Lq, max_kv_len=w.Lk)
     q, k, v = d["q"].cuda(), d["k"].cuda(), d["v"].cuda()
     out = torch.empty_like(q)
     del d
@@ -387,17 +390,17 @@ def bench_masks(steps):
     sparse = np.repeat(np.repeat(keep, 16, 0), 64, 1)[:w.Lq, :w.Lk]
     res = {"workload": w.name}
     add = np.where(sparse, 0.0, -np.inf).astype(np.float32)
-    for name, m in (("all_true", np.ones((w.Lq, w.Lk), bool)), ("block_sparse", sparse),
-                    ("block_sparse_additive", add)):
+    for name, m, p in (("all_true", np.ones((w.Lq, w.Lk), bool), plan), ("block_sparse", sparse, plan),
+                       ("block_sparse_additive", add, plan), ("block_sparse_softcap50", sparse, capped)):
         md = torch.from_numpy(m)[None, None].cuda()
         m = m if m.dtype == bool else m > -np.inf
         pairs = int((band & m).sum()) * w.B * w.Hq
-        plan.prefill(q, k, v, out, mask=md)
+        p.prefill(q, k, v, out, mask=md)
         evs = _events(steps)
         torch.cuda.synchronize()
         for a, b in evs:
             a.record()
-            plan.prefill(q, k, v, out, mask=md)
+            p.prefill(q, k, v, out, mask=md)
             b.record()
         torch.cuda.synchronize()
         ms = sum(a.elapsed_time(b) for a, b in evs) / steps

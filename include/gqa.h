@@ -247,7 +247,7 @@ typedef struct {
 } gqa_mask;
 
 /* gqa_prefill with a caller mask (arguments otherwise as gqa_prefill).  On a
- * bf16 or fp16 plan of head size 64 or 128 without softcap, a boolean mask
+ * bf16 or fp16 plan of head size 64 or 128 (with or without softcap), a boolean mask
  * whose data and strides are multiples of 8 bytes, or an additive one whose
  * data is 16-byte aligned and strides multiples of 4 elements, runs on the
  * matrix-core prefill: each wave reads its rows' entries of a 64-key tile (a
@@ -265,7 +265,7 @@ gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk
 
 /* gqa_decode with a caller mask over [B, Hq, curr, capacity] (arguments
  * otherwise as gqa_decode).  With a workspace (as gqa_decode's), a bf16/fp16
- * plan of head size 64, 128 or 256 without softcap, and a mask whose data and
+ * plan of head size 64, 128 or 256 (with or without softcap), and a mask whose data and
  * strides are multiples of 4 bytes (boolean) or 16 bytes and 4 elements
  * (additive), it runs on the matrix-core split-KV decode, each lane reading
  * its 4 entries of a 16-key unit one unit ahead.  Otherwise (or with a NULL

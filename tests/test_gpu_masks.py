@@ -38,9 +38,9 @@ def _block_sparse(seed, Lq, Lk, block=64):
 
 
 # Boolean masks with 8-byte-aligned rows (Lk % 8 == 0 here) and additive ones
-# with 16-byte-aligned rows (Lk % 4 == 0), bf16/f16, head size 64 or 128 and no
-# softcap run on the matrix-core prefill; the others on the streaming kernel.
-# Both kinds of case are listed.
+# with 16-byte-aligned rows (Lk % 4 == 0), bf16/f16 and head size 64 or 128 run
+# on the matrix-core prefill, with or without softcap; the others on the
+# streaming kernel.  Both kinds of case are listed.
 PREFILL = [
     # (dtype, B, Hq, Hkv, D, Lq, Lk, window, softcap, sink, nonpad, mask kind, mask shape)
     ("bf16", 1, 8, 2, 128, 300, 320, -1, 0.0, False, None, "sparse", "11"),   # matrix core
@@ -50,7 +50,11 @@ PREFILL = [
     ("f16", 1, 4, 4, 64, 96, 268, -1, 0.0, False, (200,), "add", "bh"),       # matrix core, tail run
     ("bf16", 2, 8, 2, 128, 200, 200, 64, 0.0, True, (200, 150), "bool", "b1"),
     ("bf16", 2, 8, 2, 128, 130, 257, -1, 0.0, False, None, "add", "1h"),
-    ("f16", 1, 4, 4, 64, 96, 96, -1, 30.0, True, None, "add", "bh"),
+    ("f16", 1, 4, 4, 64, 96, 96, -1, 30.0, True, None, "add", "bh"),           # matrix core, softcap
+    ("bf16", 2, 8, 2, 128, 200, 264, 90, 20.0, False, (264, 170), "bool", "bh"),  # matrix core, softcap
+    ("bf16", 1, 16, 4, 128, 150, 300, -1, 8.0, True, None, "add", "1h"),       # matrix core, softcap
+    ("bf16", 1, 8, 2, 128, 200, 296, 50, 15.0, False, None, "sparse", "11"),   # matrix core, softcap
+    ("bf16", 1, 8, 2, 128, 64, 130, -1, 10.0, False, None, "add", "11"),       # streaming, softcap
     ("f32", 1, 4, 2, 32, 64, 64, 16, 0.0, True, None, "bool", "11"),
     ("bf16", 1, 8, 2, 128, 300, 300, -1, 0.0, False, None, "sparse", "11"),
     ("f32", 2, 4, 2, 64, 70, 90, 20, 5.0, False, (90, 33), "add", "b1"),
@@ -93,14 +97,17 @@ def test_masked_prefill_matches_oracle(gpu, case):
 
 
 # Masks whose rows are 4-byte (boolean) / 16-byte (additive) aligned, bf16/f16
-# and no softcap run on the matrix-core decode; the others on the streaming
+# run on the matrix-core decode, with or without softcap; the others on the streaming
 # kernel.
 @pytest.mark.parametrize("dtype,D,curr,cap,kind,softcap", [
     ("bf16", 128, 1, 1024, "bool", 0.0),   # matrix core
     ("bf16", 256, 4, 600, "add", 0.0),     # matrix core
     ("f16", 64, 2, 300, "bool", 0.0),      # matrix core, last unit past the capacity
     ("bf16", 128, 3, 1500, "add", 0.0),    # matrix core, several pieces per tile
-    ("bf16", 256, 4, 600, "add", 50.0),    # streaming (softcap)
+    ("bf16", 256, 4, 600, "add", 50.0),    # matrix core, softcap
+    ("bf16", 128, 1, 1024, "bool", 30.0),  # matrix core, softcap
+    ("f16", 64, 3, 800, "add", 5.0),       # matrix core, softcap close to the logits
+    ("f16", 64, 2, 302, "add", 20.0),      # streaming (rows not 16-byte aligned)
     ("bf16", 128, 1, 1022, "bool", 0.0),   # streaming (rows not 4-byte aligned)
     ("f32", 32, 2, 100, "bool", 0.0),      # streaming (fp32)
 ])

@@ -797,9 +797,13 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       f32x4 sc = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < KQ; ++ks) sc = mma_qk<IS_BF16>(kf[ks], qf[ks], sc);
-      if constexpr (SOFTCAP) {
+      if constexpr (SOFTCAP) {  // an additive mask value enters the cap with the logit
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = a.cap_log2 * tanh_f32(sc[r] * a.scale_over_cap);
+        for (int r = 0; r < 4; ++r) {
+          float x = sc[r];
+          if constexpr (MASK == 2) x = fmaf(mf_cur[r], a.bias_mul, x);
+          sc[r] = a.cap_log2 * tanh_f32(x * a.scale_over_cap);
+        }
       }
       const bool interior = (a.window < 0 || kb >= p_last - a.window + 1) &&
                             (!a.causal || kb + kSub - 1 <= p_first) && (kb + kSub - 1 <= c_hi);
@@ -816,7 +820,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       }
       if constexpr (MASK == 2) {  // -inf (or NaN) removes the key
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = mf_cur[r] > -INFINITY ? fmaf(mf_cur[r], a.bias_mul, sc[r]) : -INFINITY;
+        for (int r = 0; r < 4; ++r)
+          sc[r] = mf_cur[r] > -INFINITY ? (SOFTCAP ? sc[r] : fmaf(mf_cur[r], a.bias_mul, sc[r])) : -INFINITY;
       }
       // online softmax: lanes n, n+16, n+32, n+48 share row n
       float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -980,11 +985,10 @@ hipError_t launch_d(const AttnArgs& a, bool softcap, const DecodeGeometry& geo, 
     return softcap ? launch_t<IS_BF16, D, true, 0, true>(a, geo, ws, stream)
                    : launch_t<IS_BF16, D, false, 0, true>(a, geo, ws, stream);
   }
-  if (a.mask_kind != 0) {  // masked launches carry no softcap (the host routes those elsewhere)
-    if (softcap) return hipErrorInvalidValue;
-    return a.mask_kind == 1 ? launch_t<IS_BF16, D, false, 1>(a, geo, ws, stream)
-                            : launch_t<IS_BF16, D, false, 2>(a, geo, ws, stream);
-  }
+  if (a.mask_kind == 1)
+    return softcap ? launch_t<IS_BF16, D, true, 1>(a, geo, ws, stream) : launch_t<IS_BF16, D, false, 1>(a, geo, ws, stream);
+  if (a.mask_kind == 2)
+    return softcap ? launch_t<IS_BF16, D, true, 2>(a, geo, ws, stream) : launch_t<IS_BF16, D, false, 2>(a, geo, ws, stream);
   return softcap ? launch_t<IS_BF16, D, true, 0>(a, geo, ws, stream) : launch_t<IS_BF16, D, false, 0>(a, geo, ws, stream);
 }
 

@@ -452,8 +452,8 @@ GQA_API gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, in
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int dtype = (int)plan->attrs.dtype;
   // Masks whose runs of 8 keys are aligned (boolean: rows at multiples of 8
-  // bytes; additive: of 16 bytes) run on the matrix-core kernel; softcap and
-  // other layouts on the streaming kernel.
+  // bytes; additive: of 16 bytes) run on the matrix-core kernel; other
+  // layouts on the streaming kernel.
   const bool small_strides = a.k_ss < (int64_t(1) << 24) && a.v_ss < (int64_t(1) << 24);
   const bool boolean = mask->kind == GQA_MASK_BOOL;
   const int64_t ealign = boolean ? 8 : 4;  // elements per aligned unit (8 or 16 bytes)
@@ -462,8 +462,9 @@ GQA_API gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, in
                        mask->stride_q % ealign == 0;
   a.bias_mul = 1.0f / plan->scale;
   if (Lk > 0 && small_strides && gqa::prefill_mfma_supported(dtype, plan->attrs.head_size) &&
-      plan->attrs.softcap == 0.0f && aligned)
-    return hip_status(gqa::launch_prefill_mfma(a, dtype, false, stream), "masked prefill launch");
+      aligned)
+    return hip_status(gqa::launch_prefill_mfma(a, dtype, plan->attrs.softcap > 0.0f, stream),
+                      "masked prefill launch");
   return hip_status(gqa::launch_attn_generic(a, dtype, stream), "masked prefill launch");
 }
 
@@ -503,15 +504,15 @@ GQA_API gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, i
   const bool boolean = mask->kind == GQA_MASK_BOOL;
   const bool aligned = reinterpret_cast<uintptr_t>(mask->data) % (boolean ? 4 : 16) == 0 &&
                        mask->stride_b % 4 == 0 && mask->stride_h % 4 == 0 && mask->stride_q % 4 == 0;
-  if (workspace != nullptr && aligned && plan->attrs.softcap == 0.0f &&
-      gqa::decode_mfma_supported(dtype, plan->attrs.head_size)) {
+  if (workspace != nullptr && aligned && gqa::decode_mfma_supported(dtype, plan->attrs.head_size)) {
     gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
     const size_t need = geo.ws_floats * sizeof(float);
     if (ws_bytes < need) return fail(GQA_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
       return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     if (geo.fits)
-      return hip_status(gqa::launch_decode_mfma(a, dtype, false, geo, reinterpret_cast<float*>(workspace), stream),
+      return hip_status(gqa::launch_decode_mfma(a, dtype, plan->attrs.softcap > 0.0f, geo,
+                                                reinterpret_cast<float*>(workspace), stream),
                         "masked decode launch");
   }
   return hip_status(gqa::launch_attn_generic(a, dtype, stream), "masked decode launch");

@@ -447,9 +447,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int sub = 0; sub < 2; ++sub) {
       const int k0 = kb + 32 * sub;
       f32x16& acc = sc[sub];
-      if constexpr (SOFTCAP) {
+      if constexpr (SOFTCAP) {  // an additive mask value enters the cap with the logit
 #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) acc[r2] = a.cap_log2 * tanh_f32(acc[r2] * a.scale_over_cap);
+        for (int r2 = 0; r2 < 16; ++r2) {
+          float x = acc[r2];
+          if constexpr (MASK == 2) x = fmaf(bias[2 * sub + (r2 >> 3)][(r2 >> 2) & 1][r2 & 3], a.bias_mul, x);
+          acc[r2] = a.cap_log2 * tanh_f32(x * a.scale_over_cap);
+        }
       }
       // masks only where the sub-tile crosses a frontier of some row of this
       // wave (or is outside all of them)
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
         for (int r2 = 0; r2 < 16; ++r2) {
           const float bv = bias[2 * sub + (r2 >> 3)][(r2 >> 2) & 1][r2 & 3];
-          acc[r2] = bv > -INFINITY ? fmaf(bv, a.bias_mul, acc[r2]) : -INFINITY;
+          acc[r2] = bv > -INFINITY ? (SOFTCAP ? acc[r2] : fmaf(bv, a.bias_mul, acc[r2])) : -INFINITY;
         }
       }
 #pragma unroll
@@ -643,7 +647,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 template <bool IS_BF16, int D>
 hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
-  if (a.mask_kind != 0 && softcap) return hipErrorInvalidValue;
   // heads per workgroup: the largest power of two that divides G, at most 8
   const int hw = std::min(a.G & -a.G, kWaves);
   const int rpw = 32 * (kWaves / hw);
@@ -651,8 +654,12 @@ hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
   const int items = a.B * a.Hkv * (a.G / hw) * nrb;
   const int per_xcd = (items + 7) / 8;
   dim3 grid(8 * per_xcd), block(64 * kWaves);
-  if (a.mask_kind == 1)
+  if (a.mask_kind == 1 && softcap)
+    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, true, 1>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
+  else if (a.mask_kind == 1)
     hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false, 1>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
+  else if (a.mask_kind == 2 && softcap)
+    hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, true, 2>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
   else if (a.mask_kind == 2)
     hipLaunchKernelGGL((prefill_mfma_kernel<IS_BF16, D, false, 2>), grid, block, 0, stream, a, nrb, items, per_xcd, hw);
   else if (softcap)
