@@ -309,6 +309,21 @@ gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capa
                           float k_scale, float v_scale,
                           void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* gqa_decode_fp8 with a caller mask over [B, Hq, curr, capacity], as for
+ * gqa_decode_masked ("Attention Kernel Design", section "Layouts and
+ * semantics": boolean or additive attention_bias broadcast over batch and
+ * heads).  An additive value is added to the scaled logit of the dequantized
+ * K (before softcap).  FP8 caches run only on the matrix-core decode, so the
+ * mask's data and strides must be multiples of 4 bytes (boolean) or 16 bytes
+ * and 4 elements (additive).
+ * Errors: as gqa_decode_fp8 and gqa_decode_masked; UNSUPPORTED for another
+ *   mask layout or a rolling cache. */
+gqa_status gqa_decode_fp8_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                 gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                 const int32_t* seqlens_k, const float* head_sink,
+                                 float k_scale, float v_scale, const gqa_mask* mask,
+                                 void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* gqa_last_error(void);
 

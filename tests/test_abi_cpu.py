@@ -254,6 +254,21 @@ def test_fp8_validation():
     st, hf = B.gqa_plan(attrs(dtype=B.GQA_F32), 4, 16, 1024)
     assert dec(hh=hf) == B.GQA_ERR_UNSUPPORTED
 
+    # with a caller mask: FP8 caches have only the matrix-core decode
+    def dm(mask, hh=h, Bn=2, ks=1.0):
+        return B.gqa_decode_fp8_masked(hh, Bn, 1, 64, t(), c8, c8, t(), s, None, ks, 1.0, mask,
+                                       ctypes.c_void_p(FAKE), ws, None)
+    ok = B.gqa_mask(FAKE, 0, 0, 64, B.GQA_MASK_BOOL)
+    assert dm(None) == B.GQA_ERR_INVALID_ARG and "mask" in B.gqa_last_error()
+    assert dm(ok, ks=0.0) == B.GQA_ERR_INVALID_ARG and "scale" in B.gqa_last_error()
+    assert dm(B.gqa_mask(FAKE + 2, 0, 0, 64, B.GQA_MASK_BOOL)) == B.GQA_ERR_UNSUPPORTED
+    assert "FP8" in B.gqa_last_error()
+    assert dm(B.gqa_mask(FAKE, 0, 0, 66, B.GQA_MASK_ADDITIVE)) == B.GQA_ERR_UNSUPPORTED
+    assert dm(B.gqa_mask(FAKE, 0, 0, 64, 3)) == B.GQA_ERR_INVALID_ARG and "kind" in B.gqa_last_error()
+    hr = plan(rolling_cache=1, local_window_size=8)
+    assert dm(ok, hh=hr) == B.GQA_ERR_UNSUPPORTED and "rolling" in B.gqa_last_error()
+    assert dm(ok, Bn=0) == B.GQA_OK
+
 
 def test_last_error_is_thread_local_and_specific():
     import threading

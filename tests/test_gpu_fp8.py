@@ -1,5 +1,6 @@
-"""FP8 (E4M3) KV caches on the GPU (gqa_append_kv_fp8, gqa_decode_fp8) against
-the oracle's FP8 cache (oracle.fp8), on the same seeded inputs.
+"""FP8 (E4M3) KV caches on the GPU (gqa_append_kv_fp8, gqa_decode_fp8,
+gqa_decode_fp8_masked) against the oracle's FP8 cache (oracle.fp8), on the
+same seeded inputs.
 
 Quantization is integer work: the cached codes must equal the oracle's bit
 for bit, over every 16-bit value and several scales.  Decode compares with
@@ -135,3 +136,46 @@ def test_fp8_decode_full_size_and_rolling(gpu):
                                  oracle.fp8.dequantize(vr.astype(np.uint8), vs), s, scale=wr.sm_scale,
                                  window=1024)
     compare(out, want, "bf16", "rolling fp8 decode")
+
+
+@pytest.mark.parametrize("dtype,D,curr,cap,kind,softcap,ks", [
+    ("bf16", 128, 1, 1024, "bool", 0.0, 0.05),
+    ("bf16", 256, 4, 600, "add", 50.0, 0.1),
+    ("f16", 64, 3, 800, "add", 0.0, 0.02),
+    ("f16", 64, 2, 300, "bool", 5.0, 0.5),
+])
+def test_fp8_decode_with_mask_matches_oracle(gpu, dtype, D, curr, cap, kind, softcap, ks):
+    """gqa_decode_fp8_masked against the oracle's attention over the
+    dequantized caches with the same mask (an additive value joins the scaled
+    logit of the dequantized K); a row whose mask removes every key is 0."""
+    B, Hq, Hkv = 3, 8, 2
+    seq = [cap - 1, 17, cap // 2]
+    w = Workload("fp8mask", "decode", dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, Lq=curr, Lk=cap,
+                 window=-1 if D != 256 else 200, softcap=softcap, smooth_softmax=True,
+                 seqlens=("list", seq), seed=700 + D + curr)
+    d = generate(w)
+    vs = 0.03
+    rng = np.random.default_rng(D + cap)
+    shape = (B, Hq, curr, cap)
+    if kind == "bool":
+        mask = torch.from_numpy(rng.random(shape) < 0.6)
+        mask[1, 3] = False
+    else:
+        m = (rng.standard_normal(shape) * 2.0).astype(np.float32)
+        m[rng.random(shape) < 0.05] = -np.inf
+        m[1, 3] = -np.inf
+        mask = torch.from_numpy(m)
+    kc0, vc0 = _codes(d["k_cache"], ks), _codes(d["v_cache"], vs)
+    plan = make_plan(w)
+    kc, vc = kc0.cuda(), vc0.cuda()
+    seq_d = d["seqlens_k"].cuda()
+    plan.append_kv_fp8(d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, seq_d, ks, vs)
+    out = plan.decode_fp8(d["q"].cuda(), kc, vc, seq_d, ks, vs, mask=mask.cuda())
+    torch.cuda.synchronize()
+    s = np.asarray(seq, dtype=np.int64)
+    kc_o, vc_o = oracle.fp8.append(kc0.numpy(), vc0.numpy(), to_f64(d["k_new"]), to_f64(d["v_new"]), s, ks, vs)
+    want = oracle.fp8.decode(to_f64(d["q"]), kc_o, vc_o, s, k_scale=ks, v_scale=vs, scale=w.sm_scale,
+                             window=w.window, softcap=softcap, smooth_softmax=True,
+                             mask=mask.numpy() if kind == "bool" else mask.numpy().astype(np.float64))
+    compare(out, want, dtype, f"fp8 masked decode {dtype} D={D} curr={curr} {kind}")
+    assert not out[1, 3].any(), "a head whose mask removes every key must give 0"

@@ -33,7 +33,7 @@ DTYPE_CODES = {"f32": GQA_F32, "f16": GQA_F16, "bf16": GQA_BF16}
 EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
             "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
-            "gqa_last_error")
+            "gqa_decode_fp8_masked", "gqa_last_error")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
@@ -121,6 +121,8 @@ def load():
     lib.gqa_append_kv_fp8.restype = ctypes.c_int
     lib.gqa_decode_fp8.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, F, F, P, S, P]
     lib.gqa_decode_fp8.restype = ctypes.c_int
+    lib.gqa_decode_fp8_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, F, F, MK, P, S, P]
+    lib.gqa_decode_fp8_masked.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -196,6 +198,14 @@ def gqa_decode_fp8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
                    v_scale, workspace, ws_bytes, stream) -> int:
     return load().gqa_decode_fp8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
                                  head_sink, k_scale, v_scale, workspace, ws_bytes, stream)
+
+
+def gqa_decode_fp8_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scale,
+                          v_scale, mask, workspace, ws_bytes, stream) -> int:
+    return load().gqa_decode_fp8_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
+                                        head_sink, k_scale, v_scale,
+                                        None if mask is None else ctypes.byref(mask),
+                                        workspace, ws_bytes, stream)
 
 
 def gqa_last_error() -> str:
@@ -422,7 +432,8 @@ class Plan:
                                 _ptr(seqlens_k), float(k_scale), float(v_scale), _stream(stream)))
 
     def decode_fp8(self, q, k_cache, v_cache, seqlens_k, k_scale, v_scale, out=None, *,
-                   head_sink=None, workspace=None, stream=None):
+                   head_sink=None, workspace=None, mask=None, stream=None):
+        """``mask``: bool or float32, broadcastable to [B, Hq, curr, capacity]."""
         import torch
         self._check_dtype(q)
         if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
@@ -432,6 +443,13 @@ class Plan:
         if workspace is None:
             workspace = self.new_workspace(q.device)
         B, _, curr, _ = q.shape
+        if mask is not None:
+            m = self.mask_view(mask, B, curr, k_cache.shape[2])
+            check(gqa_decode_fp8_masked(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_cache),
+                                        tensor_view(v_cache), tensor_view(out), _ptr(seqlens_k), _ptr(head_sink),
+                                        float(k_scale), float(v_scale), m, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+            return out
         check(gqa_decode_fp8(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_cache),
                              tensor_view(v_cache), tensor_view(out), _ptr(seqlens_k), _ptr(head_sink),
                              float(k_scale), float(v_scale), _ptr(workspace),

@@ -980,8 +980,13 @@ hipError_t launch_t(const AttnArgs& a, const DecodeGeometry& geo, float* ws, hip
 
 template <bool IS_BF16, int D>
 hipError_t launch_d(const AttnArgs& a, bool softcap, const DecodeGeometry& geo, float* ws, hipStream_t stream) {
-  if (a.kv_fp8) {  // FP8 caches: no caller mask
-    if (a.mask_kind != 0) return hipErrorInvalidValue;
+  if (a.kv_fp8) {
+    if (a.mask_kind == 1)
+      return softcap ? launch_t<IS_BF16, D, true, 1, true>(a, geo, ws, stream)
+                     : launch_t<IS_BF16, D, false, 1, true>(a, geo, ws, stream);
+    if (a.mask_kind == 2)
+      return softcap ? launch_t<IS_BF16, D, true, 2, true>(a, geo, ws, stream)
+                     : launch_t<IS_BF16, D, false, 2, true>(a, geo, ws, stream);
     return softcap ? launch_t<IS_BF16, D, true, 0, true>(a, geo, ws, stream)
                    : launch_t<IS_BF16, D, false, 0, true>(a, geo, ws, stream);
   }

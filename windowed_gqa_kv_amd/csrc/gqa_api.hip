@@ -581,10 +581,13 @@ GQA_API gqa_status gqa_append_kv_fp8(gqa_plan_t plan, int32_t B, int32_t curr, i
                     "append_kv_fp8 launch");
 }
 
-GQA_API gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
-                                  gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
-                                  const int32_t* seqlens_k, const float* head_sink, float k_scale,
-                                  float v_scale, void* workspace, size_t ws_bytes, void* hip_stream) {
+namespace {
+
+// gqa_decode_fp8 and gqa_decode_fp8_masked (mask NULL for the former).
+gqa_status decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                      gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out, const int32_t* seqlens_k,
+                      const float* head_sink, float k_scale, float v_scale, const gqa_mask* mask,
+                      void* workspace, size_t ws_bytes, void* hip_stream) {
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -599,6 +602,20 @@ GQA_API gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int6
   if ((st = check_scales(k_scale, v_scale)) != GQA_OK) return st;
   if ((st = check_sink(plan, head_sink)) != GQA_OK) return st;
   if ((st = check_ring(plan, curr, capacity)) != GQA_OK) return st;
+  if (mask != nullptr && plan->attrs.rolling_cache)
+    return fail(GQA_ERR_UNSUPPORTED, "a decode mask indexes keys by position: not with a rolling cache");
+  gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
+  if (mask != nullptr) {
+    if ((st = set_mask(a, mask)) != GQA_OK) return st;
+    // the matrix-core decode reads a lane's 4 mask entries of a unit as one
+    // aligned load; FP8 caches have no other kernel
+    const bool boolean = mask->kind == GQA_MASK_BOOL;
+    if (reinterpret_cast<uintptr_t>(mask->data) % (boolean ? 4 : 16) != 0 || mask->stride_b % 4 != 0 ||
+        mask->stride_h % 4 != 0 || mask->stride_q % 4 != 0)
+      return fail(GQA_ERR_UNSUPPORTED,
+                  "FP8 caches need a mask whose data and strides are multiples of %d bytes and 4 elements",
+                  boolean ? 4 : 16);
+  }
   if (B == 0 || curr == 0) return GQA_OK;
   if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
   const int esz = elem_size(plan->attrs.dtype);
@@ -606,12 +623,12 @@ GQA_API gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int6
   if ((st = check_tensor("k_cache", k_cache, 1)) != GQA_OK) return st;
   if ((st = check_tensor("v_cache", v_cache, 1)) != GQA_OK) return st;
   if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
-  gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
   a.seqlens = seqlens_k;
   a.head_sink = head_sink;
   a.kv_fp8 = 1;
   a.scale_log2 *= k_scale;      // scores of the codes times k_scale
   a.scale_over_cap *= k_scale;
+  a.bias_mul = 1.0f / (plan->scale * k_scale);  // an additive mask value in code-score units
   a.v_scale = v_scale;
   gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
   const size_t need = geo.ws_floats * sizeof(float);
@@ -625,6 +642,26 @@ GQA_API gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int6
   return hip_status(gqa::launch_decode_mfma(a, (int)plan->attrs.dtype, plan->attrs.softcap > 0, geo,
                                             reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(hip_stream)),
                     "decode_fp8 launch");
+}
+
+}  // namespace
+
+GQA_API gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                                  gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                  const int32_t* seqlens_k, const float* head_sink, float k_scale,
+                                  float v_scale, void* workspace, size_t ws_bytes, void* hip_stream) {
+  return decode_fp8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scale, v_scale,
+                    nullptr, workspace, ws_bytes, hip_stream);
+}
+
+GQA_API gqa_status gqa_decode_fp8_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                         gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                         const int32_t* seqlens_k, const float* head_sink, float k_scale,
+                                         float v_scale, const gqa_mask* mask, void* workspace, size_t ws_bytes,
+                                         void* hip_stream) {
+  if (mask == nullptr) return fail(GQA_ERR_INVALID_ARG, "mask is NULL");
+  return decode_fp8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scale, v_scale,
+                    mask, workspace, ws_bytes, hip_stream);
 }
 
 GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }
