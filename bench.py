@@ -443,7 +443,10 @@ def bench_masks(steps):
 def bench_fp8(reps):
     """The headline decode on FP8 (E4M3) caches (gqa_decode_fp8): graphs of
     back-to-back decodes over 16 cache replicas (1 GiB), HIP events around the
-    replays.  Bytes: the K/V rows at one byte per element, Q and O."""
+    replays.  Bytes: the K/V rows at one byte per element, Q and O.  The same
+    graphs again through gqa_decode_fp8_masked with a random boolean
+    [B, Hq, 1, capacity] mask (90% of the keys kept)."""
+    import numpy as np
     import torch
     from windowed_gqa_kv_amd import binding, work
     from windowed_gqa_kv_amd.inputs import WORKLOADS, generate
@@ -466,24 +469,30 @@ def bench_fp8(reps):
         plan.append_kv_fp8(kn, vn, kc, vc, seq, ks, vs)
         plan.decode_fp8(q, kc, vc, seq, ks, vs, out, workspace=ws)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for kc, vc in caches:
-            plan.decode_fp8(q, kc, vc, seq, ks, vs, out, workspace=ws)
-    g.replay()
-    torch.cuda.synchronize()
-    ev = _events(reps)
-    for a, b in ev:
-        a.record()
+    md = torch.from_numpy(np.random.default_rng(12).random((w.B, w.Hq, 1, w.Lk)) < 0.9).cuda()
+    times = []
+    for mask in (None, md):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for kc, vc in caches:
+                plan.decode_fp8(q, kc, vc, seq, ks, vs, out, workspace=ws, mask=mask)
         g.replay()
-        b.record()
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / (reps * R)
+        torch.cuda.synchronize()
+        ev = _events(reps)
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        times.append(sum(a.elapsed_time(b) for a, b in ev) / (reps * R))
+        del g
+    ms, ms_masked = times
     s = d["seqlens_k"].numpy().astype("int64")
     b = work.decode_bytes(s, w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window, kv_dtype="fp8")
     return {"workload": w.name, "kernel": "decode_kernel (FP8 caches)", "kernel_ms": round(ms, 5),
             "bytes_per_launch": b, "achieved": round(b / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
-            "frac": round(b / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "frac": round(b / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bool_mask_kernel_ms": round(ms_masked, 5)}
 
 
 def cpu_baseline(w, d, budget_s=12.0):
