@@ -110,15 +110,21 @@ typedef struct {
 gqa_status gqa_plan(const gqa_attrs* attrs, int32_t max_batch, int32_t max_q_len,
                     int64_t max_kv_len, gqa_plan_t* out_plan);
 
-/* Release a plan (NULL is ignored).  Must not race with calls using it. */
+/* Release a plan (NULL is ignored).  Must not race with calls using it.
+ * The plan is the host-side descriptor of "Attention Kernel Design", section
+ * "Descriptor and invocation plan"; it owns no device memory. */
 void gqa_plan_destroy(gqa_plan_t plan);
 
 /* Bytes of device workspace gqa_decode needs at the plan's maxima: per-row-
- * tile arrival counters followed by the split-KV partial results.  The
- * workspace must be zero-filled once before its first gqa_decode call; every
- * completed call leaves the counters at zero again, so it can be reused by
- * later calls (of any plan) without clearing.  gqa_prefill and gqa_append_kv
- * need none.  0 for NULL. */
+ * tile arrival counters (a fixed region of 2048 32-bit words at the front)
+ * followed by the split-KV partial results (running max, denominator and
+ * unnormalized output of each piece of the key range, merged by log-sum-exp:
+ * the streaming recurrence of "Attention Kernel Design", section "Compute
+ * paths", cut into independent key ranges).  The workspace must be
+ * zero-filled once before its first gqa_decode call; every completed call
+ * leaves the counters at zero again, so it can be reused by later calls (of
+ * any plan and shape) without clearing.  gqa_prefill and gqa_append_kv need
+ * none.  0 for NULL. */
 size_t gqa_workspace_size(gqa_plan_t plan);
 
 /* Prompt attention on an empty past ("Attention Kernel Design", sections
@@ -324,7 +330,12 @@ gqa_status gqa_decode_fp8_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64
                                  float k_scale, float v_scale, const gqa_mask* mask,
                                  void* workspace, size_t ws_bytes, void* hip_stream);
 
-/* Message for the last non-OK status returned on this thread ("" if none). */
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * Every rejection names the argument and the rule it breaks: the "rejected
+ * with specific messages" convention of "onnx: import GroupQueryAttention
+ * decode steps and its internal rotary", section "What changed", and the
+ * explicit failure of invalid pairings of "Attention Kernel Design", section
+ * "Scheduling, precision, and invariants". */
 const char* gqa_last_error(void);
 
 #ifdef __cplusplus

@@ -69,18 +69,50 @@ def test_workload4_spec_decode(gpu):
     _say(f"w4 err {compare(out, want, 'bf16', 'w4')}")
 
 
-def test_workload5_large_gqa_prefill_sampled(gpu):
+def _w5_rows():
+    """The large prefill's sampled rows: rows 0-127, the window edge
+    (8190-8194), batch 1's padding edge (24570-24582), the last rows that
+    still see batch 1's last key 24575 (up to 24575 + 8191 = 32766), the last
+    128 rows (row 32767 of batch 1 sees no key) and 384 seeded random rows --
+    about 640 rows for every (batch, head)."""
+    rng = np.random.default_rng(55)
+    rows = set(range(128)) | set(range(8190, 8195)) | set(range(24570, 24583))
+    rows |= set(range(32766 - 40, 32767)) | set(range(32768 - 128, 32768))
+    rows |= set(rng.integers(128, 32768 - 128, 384).tolist())
+    rows = np.array(sorted(rows))
+    assert rows.min() >= 0 and rows.max() < 32768
+    return rows
+
+
+@pytest.fixture(scope="module")
+def w5_run(gpu):
+    """One run of the large GQA prefill; keeps the sampled rows of every head."""
     w = WORKLOADS[5]
     d = generate(w)
     got = gpu_prefill(w, d)
-    rows = _sample_rows(w.Lq, [8191, 24576, 24576 + 8191, 32767], seed=5, n_rand=24)
-    heads = [0, 7, 8, 21, 42, 63]
-    want = oracle_prefill(w, d, rows=rows, heads=heads)
-    g = got[:, heads][:, :, rows]
-    wnt = np.stack([want[h] for h in heads], axis=1)
-    _say(f"w5 err {compare(g, wnt, 'bf16', 'w5')}")
+    rows = _w5_rows()
+    assert 0 <= rows.min() and rows.max() < w.Lq  # indexes on the GPU: checked on the host
+    sample = got[:, :, torch.from_numpy(rows).cuda()].cpu()
+    empty_row_nonzero = torch.count_nonzero(got[1, :, 32767]).item()
+    del got
+    torch.cuda.empty_cache()
+    _say(f"w5: {len(rows)} rows per (batch, head) sampled")
+    return w, d, rows, sample, empty_row_nonzero
+
+
+@pytest.mark.parametrize("h0", range(0, 64, 8))
+def test_workload5_large_gqa_prefill_sampled(w5_run, h0):
+    """Every (batch, head) of the large prefill on ~640 rows against the
+    oracle, eight heads per test (the oracle takes a few seconds per head)."""
+    from concurrent.futures import ThreadPoolExecutor
+    w, d, rows, sample, empty_row_nonzero = w5_run
+    heads = list(range(h0, h0 + 8))
+    with ThreadPoolExecutor(4) as ex:
+        parts = list(ex.map(lambda h: oracle_prefill(w, d, rows=rows, heads=[h])[h], heads))
+    wnt = np.stack(parts, axis=1)
+    _say(f"w5 heads {h0}-{h0 + 7} err {compare(sample[:, heads], wnt, 'bf16', f'w5 heads {h0}..')}")
     # batch 1 row 32767 sees no key at all
-    assert torch.count_nonzero(got[1, :, 32767]).item() == 0
+    assert empty_row_nonzero == 0
 
 
 # --------------------------------------------------------------------------
@@ -255,6 +287,29 @@ def test_decode_workspace_reuse_across_shapes(gpu):
             plan.append_kv(d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, seq)
             out = plan.decode(d["q"].cuda(), kc, vc, seq, workspace=ws,
                               head_sink=None if d["head_sink"] is None else d["head_sink"].cuda())
+            _t.cuda.synchronize()
+            compare(out, oracle_decode(w, d), "bf16", f"reuse {rep} {w}")
+
+
+def test_decode_workspace_reuse_more_tiles_after_fewer(gpu):
+    """A call with many (batch, KV head, 16-row) tiles after one with few, on the
+    same workspace and without clearing it: the arrival counters sit in a
+    fixed region at the front, so the larger call never reads the smaller
+    call's partial results as counters."""
+    import torch as _t
+    small = Workload("reuse_s", "decode", "bf16", B=3, Hq=8, Hkv=2, D=128, Lq=1, Lk=600, window=-1,
+                     seqlens=("list", [599, 300, 5]), seed=31)
+    big = Workload("reuse_b", "decode", "bf16", B=16, Hq=32, Hkv=8, D=128, Lq=1, Lk=600, window=-1,
+                   smooth_softmax=True, seqlens=("uniform", 1, 600), seed=32)
+    plans = [make_plan(w) for w in (small, big)]
+    ws = _t.zeros(max(p.workspace_size() for p in plans), dtype=_t.uint8, device="cuda")
+    for rep in range(2):
+        for w, plan in zip((small, big), plans):
+            d = generate(w)
+            kc, vc = d["k_cache"].cuda(), d["v_cache"].cuda()
+            seq = d["seqlens_k"].cuda()
+            plan.append_kv(d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, seq)
+            out = plan.decode(d["q"].cuda(), kc, vc, seq, workspace=ws)
             _t.cuda.synchronize()
             compare(out, oracle_decode(w, d), "bf16", f"reuse {rep} {w}")
 

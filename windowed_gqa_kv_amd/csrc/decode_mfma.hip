@@ -52,7 +52,7 @@ constexpr int kRowsPerTile = 16;
 constexpr int kSub = 16;              // keys per unit (MFMA M)
 constexpr int kWaves = 4;
 constexpr float kRescaleLog2 = 8.0f;
-constexpr int kMaxTiles = 2048;       // row tiles per call on this path
+constexpr int kMaxTiles = kDecodeMaxTiles;  // row tiles per call on this path
 constexpr int kMaxGrid = 2048;        // workgroups per launch (upper bound)
 constexpr int kCachedTiles = 160;     // tiles whose lengths the setup keeps in LDS
 constexpr int kNonTemporal = 2;       // cache-policy bits of a load: nt (gfx950)
@@ -964,38 +964,69 @@ int resident_grid(K kernel) {
   return std::max(1, std::min(kMaxGrid, cus * per_cu));
 }
 
-template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8 = false>
-hipError_t launch_t(const AttnArgs& a, const DecodeGeometry& geo, float* ws, hipStream_t stream) {
-  auto kernel = decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8>;
-  static int grid_cache[16] = {0};  // per device; a benign race computes the same value
+// The grid of one kernel instance on the current device (computed once per
+// device; a benign race computes the same value).
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8>
+int grid_of() {
+  static int grid_cache[16] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   int G = grid_cache[dev];
-  if (G == 0) G = grid_cache[dev] = resident_grid(kernel);
-  unsigned* counters = reinterpret_cast<unsigned*>(ws);
-  float* part = ws + geo.counter_floats;
-  hipLaunchKernelGGL(kernel, dim3(G), dim3(256), 0, stream, a, geo.rows, geo.row_tiles, part, counters);
-  return hipGetLastError();
+  if (G == 0) G = grid_cache[dev] = resident_grid(decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8>);
+  return G;
 }
 
-template <bool IS_BF16, int D>
-hipError_t launch_d(const AttnArgs& a, bool softcap, const DecodeGeometry& geo, float* ws, hipStream_t stream) {
+// The instance a call runs on, as compile-time arguments of op.run<...>().
+template <bool IS_BF16, int D, typename Op>
+auto visit_d(const AttnArgs& a, bool softcap, const Op& op) {
   if (a.kv_fp8) {
     if (a.mask_kind == 1)
-      return softcap ? launch_t<IS_BF16, D, true, 1, true>(a, geo, ws, stream)
-                     : launch_t<IS_BF16, D, false, 1, true>(a, geo, ws, stream);
+      return softcap ? op.template run<IS_BF16, D, true, 1, true>() : op.template run<IS_BF16, D, false, 1, true>();
     if (a.mask_kind == 2)
-      return softcap ? launch_t<IS_BF16, D, true, 2, true>(a, geo, ws, stream)
-                     : launch_t<IS_BF16, D, false, 2, true>(a, geo, ws, stream);
-    return softcap ? launch_t<IS_BF16, D, true, 0, true>(a, geo, ws, stream)
-                   : launch_t<IS_BF16, D, false, 0, true>(a, geo, ws, stream);
+      return softcap ? op.template run<IS_BF16, D, true, 2, true>() : op.template run<IS_BF16, D, false, 2, true>();
+    return softcap ? op.template run<IS_BF16, D, true, 0, true>() : op.template run<IS_BF16, D, false, 0, true>();
   }
   if (a.mask_kind == 1)
-    return softcap ? launch_t<IS_BF16, D, true, 1>(a, geo, ws, stream) : launch_t<IS_BF16, D, false, 1>(a, geo, ws, stream);
+    return softcap ? op.template run<IS_BF16, D, true, 1, false>() : op.template run<IS_BF16, D, false, 1, false>();
   if (a.mask_kind == 2)
-    return softcap ? launch_t<IS_BF16, D, true, 2>(a, geo, ws, stream) : launch_t<IS_BF16, D, false, 2>(a, geo, ws, stream);
-  return softcap ? launch_t<IS_BF16, D, true, 0>(a, geo, ws, stream) : launch_t<IS_BF16, D, false, 0>(a, geo, ws, stream);
+    return softcap ? op.template run<IS_BF16, D, true, 2, false>() : op.template run<IS_BF16, D, false, 2, false>();
+  return softcap ? op.template run<IS_BF16, D, true, 0, false>() : op.template run<IS_BF16, D, false, 0, false>();
 }
+template <typename Op, typename R>
+R visit(const AttnArgs& a, int dtype, bool softcap, const Op& op, R unsupported) {
+  if (dtype == kBF16) {
+    if (a.D == 128) return visit_d<true, 128>(a, softcap, op);
+    if (a.D == 256) return visit_d<true, 256>(a, softcap, op);
+    if (a.D == 64) return visit_d<true, 64>(a, softcap, op);
+  } else if (dtype == kF16) {
+    if (a.D == 128) return visit_d<false, 128>(a, softcap, op);
+    if (a.D == 256) return visit_d<false, 256>(a, softcap, op);
+    if (a.D == 64) return visit_d<false, 64>(a, softcap, op);
+  }
+  return unsupported;
+}
+
+struct LaunchOp {
+  const AttnArgs& a;
+  const DecodeGeometry& geo;
+  float* ws;
+  hipStream_t stream;
+  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8>
+  hipError_t run() const {
+    const int G = grid_of<IS_BF16, D, SOFTCAP, MASK, KV8>();
+    unsigned* counters = reinterpret_cast<unsigned*>(ws);
+    float* part = ws + geo.counter_floats;
+    hipLaunchKernelGGL((decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8>), dim3(G), dim3(256), 0, stream, a, geo.rows,
+                       geo.row_tiles, part, counters);
+    return hipGetLastError();
+  }
+};
+struct GridOp {
+  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8>
+  int run() const {
+    return grid_of<IS_BF16, D, SOFTCAP, MASK, KV8>();
+  }
+};
 
 }  // namespace
 
@@ -1008,28 +1039,26 @@ DecodeGeometry decode_geometry(int B, int Hkv, int G, int curr, int head_size) {
   geo.rows = G * curr;
   geo.row_tiles = (geo.rows + kRowsPerTile - 1) / kRowsPerTile;
   geo.tiles = (int64_t)B * Hkv * geo.row_tiles;
-  // one 32-bit arrival counter per row tile (256-byte aligned), then one
-  // partial per piece: at most grid + tiles pieces per call
-  geo.counter_floats = (size_t)(geo.tiles + 63) / 64 * 64;
-  geo.ws_floats = geo.counter_floats +
-                  (size_t)(kMaxGrid + geo.tiles) * (size_t)(kRowsPerTile * head_size + 2 * kRowsPerTile);
+  // One 32-bit arrival counter per row tile in a region of fixed size (the
+  // most tiles a launch takes), so that calls of any shape find their
+  // counters at zero in a shared workspace; then one partial per piece, at
+  // most grid + tiles pieces per call.
+  geo.counter_floats = kMaxTiles;
+  geo.part_floats = (size_t)(kRowsPerTile * head_size + 2 * kRowsPerTile);
+  geo.ws_floats = geo.counter_floats + (size_t)(kMaxGrid + geo.tiles) * geo.part_floats;
   geo.fits = geo.tiles <= kMaxTiles;
   return geo;
+}
+
+size_t decode_mfma_scratch_floats(const AttnArgs& a, int dtype, bool softcap, const DecodeGeometry& geo) {
+  const int grid = visit(a, dtype, softcap, GridOp{}, 0);
+  return geo.counter_floats + (size_t)(grid + geo.tiles) * geo.part_floats;
 }
 
 hipError_t launch_decode_mfma(const AttnArgs& a, int dtype, bool softcap, const DecodeGeometry& geo,
                               float* ws, hipStream_t stream) {
   if (a.B == 0 || a.Lq == 0) return hipSuccess;
-  if (dtype == kBF16) {
-    if (a.D == 128) return launch_d<true, 128>(a, softcap, geo, ws, stream);
-    if (a.D == 256) return launch_d<true, 256>(a, softcap, geo, ws, stream);
-    if (a.D == 64) return launch_d<true, 64>(a, softcap, geo, ws, stream);
-  } else if (dtype == kF16) {
-    if (a.D == 128) return launch_d<false, 128>(a, softcap, geo, ws, stream);
-    if (a.D == 256) return launch_d<false, 256>(a, softcap, geo, ws, stream);
-    if (a.D == 64) return launch_d<false, 64>(a, softcap, geo, ws, stream);
-  }
-  return hipErrorInvalidValue;
+  return visit(a, dtype, softcap, LaunchOp{a, geo, ws, stream}, hipErrorInvalidValue);
 }
 
 }  // namespace gqa

@@ -31,13 +31,18 @@ struct DecodeGeometry {
   int row_tiles;          // ceil(rows / 16)
   int64_t tiles;          // B * Hkv * row_tiles
   size_t counter_floats;  // leading workspace words holding the arrival counters
-  size_t ws_floats;
+  size_t part_floats;     // words of one piece's partial result
+  size_t ws_floats;       // workspace words at the largest grid a launch may take
   bool fits;              // tiles within the kernel's per-call limit
 };
 bool decode_mfma_supported(int dtype, int head_size);
 DecodeGeometry decode_geometry(int B, int Hkv, int G, int curr, int head_size);
 hipError_t launch_decode_mfma(const AttnArgs& a, int dtype, bool softcap,
                               const DecodeGeometry& geo, float* ws, hipStream_t stream);
+// Workspace words the launch above uses on the current device (its resident
+// grid instead of the largest one): at most geo.ws_floats.
+size_t decode_mfma_scratch_floats(const AttnArgs& a, int dtype, bool softcap, const DecodeGeometry& geo);
+constexpr int kDecodeMaxTiles = 2048;  // arrival counters at the front of every decode workspace
 
 // KV-cache append: copy curr rows per (batch, KV head) to slots
 // total_b - curr ... total_b - 1 of the cache.
