@@ -154,3 +154,62 @@ def to_f64(t):
     if t is None:
         return None
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def staircase(n: int, step: float, period: int) -> np.ndarray:
+    """Logit levels of a staircase over key positions 0..n-1: position j sits
+    on level floor(j / period), at height step * level (nats)."""
+    return step * (np.arange(n) // period).astype(np.float64)
+
+
+def bursts(n: int, height: float, period: int, width: int, offset: int = 0) -> np.ndarray:
+    """Logit levels that are 0 except for bursts of `width` positions at
+    `height` (nats) ending every `period` positions (shifted by `offset`)."""
+    j = np.arange(n) + offset
+    return np.where(j % period >= period - width, height, 0.0)
+
+
+def shape_logits(w: Workload, d: dict, levels: np.ndarray, seed: int, *, a: float = 1.0,
+                 q_noise: float = 0.1, k_noise: float = 0.3, v_level: float = 0.7,
+                 v_noise: float = 0.5, flip: Optional[np.ndarray] = None) -> dict:
+    """Inputs whose scaled logits follow a prescribed profile over key positions.
+
+    Every query row is a * u plus noise and key position j is
+    levels[j] / (a * |u|^2 * scale) * u plus noise, for one fixed +-1 vector u,
+    so that the scaled logit of any query against position j is about
+    levels[j] nats (plus noise of a few tenths).  Values are +-v_level plus
+    noise, the sign given by `flip` (default: alternating with the level's
+    rank), so that the result depends on how the softmax weighs different
+    levels.  Decode inputs place new token t of batch b at position
+    seqlens_k[b] + 1 - curr + t.  The rest of `d` (lengths, sinks) is kept.
+    This designs inputs; it computes no attention."""
+    rng = np.random.default_rng(seed)
+    D, scale = w.D, w.sm_scale
+    u = rng.choice([-1.0, 1.0], size=D)
+    b_of = levels / (a * D * scale)                       # u-coefficient of each position
+    if flip is None:
+        _, rank = np.unique(levels, return_inverse=True)
+        flip = np.where(rank % 2 == 0, 1.0, -1.0)
+    dt = TORCH_DTYPES[w.dtype]
+
+    def rows(shape, coef, noise, sign=None):
+        if sign is not None:
+            x = sign[..., None] * v_level + noise * rng.standard_normal(shape + (D,))
+        else:
+            x = coef[..., None] * u + noise * rng.standard_normal(shape + (D,))
+        return torch.from_numpy(x.astype(np.float32)).to(dt)
+
+    out = dict(d)
+    out["q"] = rows((w.B, w.Hq, w.Lq), np.full((w.B, w.Hq, w.Lq), a), q_noise)
+    kv = (w.B, w.Hkv, w.Lk)
+    pos = np.broadcast_to(np.arange(w.Lk), kv)
+    k_name, v_name = ("k", "v") if w.kind == "prefill" else ("k_cache", "v_cache")
+    out[k_name] = rows(kv, b_of[pos], k_noise)
+    out[v_name] = rows(kv, None, v_noise, sign=flip[pos])
+    if w.kind == "decode":
+        s = d["seqlens_k"].numpy().astype(np.int64)
+        npos = (s + 1 - w.Lq)[:, None, None] + np.arange(w.Lq)[None, None, :]
+        npos = np.broadcast_to(np.clip(npos, 0, w.Lk - 1), (w.B, w.Hkv, w.Lq))
+        out["k_new"] = rows((w.B, w.Hkv, w.Lq), b_of[npos], k_noise)
+        out["v_new"] = rows((w.B, w.Hkv, w.Lq), None, v_noise, sign=flip[npos])
+    return out
