@@ -263,8 +263,38 @@ def _dtype_code(t):
     return _TORCH_CODE[t.dtype]
 
 
+def _need(cond, msg, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
+def _aux(name, t, dtype, n):
+    """An optional per-batch or per-head array: dtype and at least n elements."""
+    if t is None:
+        return
+    _need(t.dtype == dtype, f"{name} must be {dtype} (got {t.dtype})", TypeError)
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(t.numel() >= n, f"{name} needs at least {n} elements (got {t.numel()})")
+
+
+def _same_device(ref, **ts):
+    """Every tensor on ref's device, which must be a GPU: the library reads
+    them as device pointers."""
+    _need(ref.device.type == "cuda", f"tensors must be on a GPU (got {ref.device})")
+    for name, t in ts.items():
+        if t is not None:
+            _need(t.device == ref.device, f"{name} is on {t.device}, not on {ref.device}")
+
+
 class Plan:
-    """An immutable attention plan (``gqa_plan``) driven with torch tensors."""
+    """An immutable attention plan (``gqa_plan``) driven with torch tensors.
+
+    Every call checks its tensors' shapes against the plan (head counts, head
+    size), the dtypes and lengths of the per-batch and per-head arrays
+    (seqlens_k int32 [B], nonpad_kv_seqlen int64 [B], head_sink float32 [Hq])
+    and that all of them live on the GPU of q, before any pointer reaches the
+    library; a mismatch raises ValueError or TypeError.
+    """
 
     def __init__(self, num_heads: int, kv_num_heads: int, head_size: int, *, dtype: str,
                  scale: float = 0.0, local_window_size: int = -1, softcap: float = 0.0,
@@ -304,6 +334,33 @@ class Plan:
             if t is not None and _dtype_code(t) != want:
                 raise TypeError(f"tensor dtype {t.dtype} does not match the plan's {self.dtype}")
 
+    def _rows(self, name, t, heads, layout="bhsd"):
+        """(B, L) of a [B, H, L, D] (or [B, L, H*D]) tensor with the plan's head
+        count and head size."""
+        if layout == "bhsd":
+            _need(t.dim() == 4, f"{name} must be 4-D [B, H, L, D]")
+            _need(t.shape[1] == heads and t.shape[3] == self.head_size,
+                  f"{name} has shape {tuple(t.shape)}: expected [B, {heads}, L, {self.head_size}]")
+            return t.shape[0], t.shape[2]
+        _need(t.dim() == 3, f"{name} must be 3-D [B, L, H*D]")
+        _need(t.shape[2] == heads * self.head_size,
+              f"{name} has shape {tuple(t.shape)}: expected [B, L, {heads * self.head_size}]")
+        return t.shape[0], t.shape[1]
+
+    def _caches(self, B, k_cache, v_cache, elem=None):
+        """Capacity of a [>= B, Hkv, capacity, D] cache pair."""
+        Bk, cap = self._rows("k_cache", k_cache, self.kv_num_heads)
+        _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+        _need(Bk >= B, f"the caches hold {Bk} batches, fewer than B = {B}")
+        if elem is not None:
+            _need(k_cache.dtype == elem and v_cache.dtype == elem, f"caches must be {elem}", TypeError)
+        return cap
+
+    def _workspace(self, ws):
+        _need(ws.is_contiguous(), "workspace must be contiguous")
+        _need(ws.numel() * ws.element_size() >= self.workspace_size(),
+              f"workspace of {self.workspace_size()} bytes needed")
+
     def mask_view(self, mask, B, Lq, Lk) -> gqa_mask:
         """gqa_mask for a bool (True attends) or float32 (additive) tensor
         broadcastable to [B, Hq, Lq, Lk]."""
@@ -326,7 +383,16 @@ class Plan:
         """q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (layout "bhsd") or [B,L,H*D] ("bshd").
         ``mask``: bool or float32, broadcastable to [B, Hq, Lq, Lk]."""
         import torch
-        self._check_dtype(q, k, v)
+        self._check_dtype(q, k, v, out)
+        B, Lq = self._rows("q", q, self.num_heads, layout)
+        Bk, Lk = self._rows("k", k, self.kv_num_heads, layout)
+        _need(tuple(v.shape) == tuple(k.shape), "k and v differ in shape")
+        _need(Bk == B, f"q has {B} batches, k has {Bk}")
+        _need(out is None or tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+        _aux("nonpad_kv_seqlen", nonpad_kv_seqlen, torch.int64, B)
+        _aux("head_sink", head_sink, torch.float32, self.num_heads)
+        _same_device(q, k=k, v=v, out=out, nonpad_kv_seqlen=nonpad_kv_seqlen, head_sink=head_sink,
+                     mask=mask)
         if out is None:
             out = torch.empty_like(q)
         if layout == "bhsd":
@@ -348,8 +414,14 @@ class Plan:
         return out
 
     def append_kv(self, k_new, v_new, k_cache, v_cache, seqlens_k, *, stream=None):
+        import torch
         self._check_dtype(k_new, v_new, k_cache, v_cache)
-        B, _, curr, _ = k_new.shape
+        B, curr = self._rows("k_new", k_new, self.kv_num_heads)
+        _need(tuple(v_new.shape) == tuple(k_new.shape), "k_new and v_new differ in shape")
+        self._caches(B, k_cache, v_cache)
+        _need(seqlens_k is not None, "seqlens_k is required")
+        _aux("seqlens_k", seqlens_k, torch.int32, B)
+        _same_device(k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, seqlens_k=seqlens_k)
         check(gqa_append_kv(self._h, B, curr, k_cache.shape[2], tensor_view(k_new),
                             tensor_view(v_new), tensor_view(k_cache), tensor_view(v_cache),
                             _ptr(seqlens_k), _stream(stream)))
@@ -358,7 +430,8 @@ class Plan:
                workspace=None, mask=None, stream=None):
         """``mask``: bool or float32, broadcastable to [B, Hq, curr, capacity]."""
         import torch
-        self._check_dtype(q, k_cache, v_cache)
+        self._check_dtype(q, k_cache, v_cache, out)
+        self._decode_args(q, k_cache, v_cache, seqlens_k, out, head_sink, workspace, mask)
         if out is None:
             out = torch.empty_like(q)
         if mask is not None:
@@ -381,6 +454,19 @@ class Plan:
                          _stream(stream)))
         return out
 
+    def _decode_args(self, q, k_cache, v_cache, seqlens_k, out, head_sink, workspace, mask, elem=None):
+        import torch
+        B, _ = self._rows("q", q, self.num_heads)
+        self._caches(B, k_cache, v_cache, elem)
+        _need(out is None or tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+        _need(seqlens_k is not None, "seqlens_k is required")
+        _aux("seqlens_k", seqlens_k, torch.int32, B)
+        _aux("head_sink", head_sink, torch.float32, self.num_heads)
+        if workspace is not None:
+            self._workspace(workspace)
+        _same_device(q, k_cache=k_cache, v_cache=v_cache, seqlens_k=seqlens_k, out=out,
+                     head_sink=head_sink, workspace=workspace, mask=mask)
+
     @staticmethod
     def _tables(cos, sin):
         import torch
@@ -394,9 +480,12 @@ class Plan:
     def apply_rotary(self, x, pos0, cos, sin, out=None, *, stream=None):
         """Rotary embedding of x [B, H, L, D] at positions pos0 + l (out may be x)."""
         import torch
-        self._check_dtype(x)
+        self._check_dtype(x, out)
+        _need(x.dim() == 4 and x.shape[3] == self.head_size, f"x must be [B, H, L, {self.head_size}]")
+        _need(out is None or tuple(out.shape) == tuple(x.shape), "out must have x's shape")
         if cos.shape[1] * 2 != self.head_size:
             raise ValueError("rotary tables need head_size / 2 columns")
+        _same_device(x, out=out, cos=cos, sin=sin)
         if out is None:
             out = torch.empty_like(x)
         B, H, L, _ = x.shape
@@ -408,9 +497,19 @@ class Plan:
                          q_rot=None, *, stream=None):
         """One decode step's append with rotary; returns the rotated q (q_rot may be q)."""
         import torch
-        self._check_dtype(q, k_new, v_new, k_cache, v_cache)
+        self._check_dtype(q, k_new, v_new, k_cache, v_cache, q_rot)
+        Bq, curr_q = self._rows("q", q, self.num_heads)
+        B, curr = self._rows("k_new", k_new, self.kv_num_heads)
+        _need((Bq, curr_q) == (B, curr), "q and k_new differ in batch or step length")
+        _need(tuple(v_new.shape) == tuple(k_new.shape), "k_new and v_new differ in shape")
+        _need(q_rot is None or tuple(q_rot.shape) == tuple(q.shape), "q_rot must have q's shape")
+        self._caches(B, k_cache, v_cache)
+        _need(seqlens_k is not None, "seqlens_k is required")
+        _aux("seqlens_k", seqlens_k, torch.int32, B)
         if cos.shape[1] * 2 != self.head_size:
             raise ValueError("rotary tables need head_size / 2 columns")
+        _same_device(q, q_rot=q_rot, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+                     seqlens_k=seqlens_k, cos=cos, sin=sin)
         if q_rot is None:
             q_rot = torch.empty_like(q)
         B, _, curr, _ = k_new.shape
@@ -426,7 +525,12 @@ class Plan:
         self._check_dtype(k_new, v_new)
         if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
             raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
-        B, _, curr, _ = k_new.shape
+        B, curr = self._rows("k_new", k_new, self.kv_num_heads)
+        _need(tuple(v_new.shape) == tuple(k_new.shape), "k_new and v_new differ in shape")
+        self._caches(B, k_cache, v_cache)
+        _need(seqlens_k is not None, "seqlens_k is required")
+        _aux("seqlens_k", seqlens_k, torch.int32, B)
+        _same_device(k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, seqlens_k=seqlens_k)
         check(gqa_append_kv_fp8(self._h, B, curr, k_cache.shape[2], tensor_view(k_new),
                                 tensor_view(v_new), tensor_view(k_cache), tensor_view(v_cache),
                                 _ptr(seqlens_k), float(k_scale), float(v_scale), _stream(stream)))
@@ -435,9 +539,10 @@ class Plan:
                    head_sink=None, workspace=None, mask=None, stream=None):
         """``mask``: bool or float32, broadcastable to [B, Hq, curr, capacity]."""
         import torch
-        self._check_dtype(q)
+        self._check_dtype(q, out)
         if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
             raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+        self._decode_args(q, k_cache, v_cache, seqlens_k, out, head_sink, workspace, mask, torch.uint8)
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
