@@ -25,7 +25,9 @@
  *
  * Conventions shared by every entry point.
  *   Ownership:  every device buffer belongs to the caller.  The library never
- *               allocates device memory; it owns only the host-side plan.
+ *               allocates device memory; it owns only the host-side plan and
+ *               the static decode scratch array of gqa_decode_noalloc (part of
+ *               its code object, one per GPU).
  *   Asynchrony: calls enqueue work on `hip_stream` (a hipStream_t; NULL = the
  *               default stream) and return; GQA_OK means "enqueued".
  *   Validation: everything checkable on the host is checked before any launch.
@@ -181,6 +183,24 @@ gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity
                       gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
                       const int32_t* seqlens_k, const float* head_sink,
                       void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* gqa_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The split-KV partials and arrival counters live
+ * in a static device array of the library, 16 MiB per GPU, held by each GPU
+ * the library runs on until the process ends; its address is looked up on
+ * the first call on a device, which also clears the counters with a small
+ * kernel on `hip_stream`.  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library call.  All calls on one GPU share that array, so calls
+ * that overlap in time on one GPU (other streams, other threads) race and
+ * must not be issued; consecutive calls on one stream are fine.  Arguments,
+ * results and the other errors are those of gqa_decode.
+ * Errors: as gqa_decode, and CAPACITY when a call needs more scratch than the
+ *   array holds (about 1500 row tiles of 16 query rows at head size 128, 760
+ *   at 256; such calls need gqa_decode with a workspace). */
+gqa_status gqa_decode_noalloc(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                              gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                              const int32_t* seqlens_k, const float* head_sink, void* hip_stream);
 
 /* Rotary position tables supplied by the caller ("onnx: import
  * GroupQueryAttention decode steps and its internal rotary", section "What

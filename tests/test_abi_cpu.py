@@ -154,6 +154,25 @@ def test_decode_validation():
     assert dec(curr=0) == B.GQA_OK
 
 
+def test_decode_noalloc_validation():
+    """gqa_decode_noalloc checks its arguments like gqa_decode, before it
+    looks up its scratch array or launches anything."""
+    h = plan()
+    s = ctypes.c_void_p(FAKE)
+    def dec(hh=h, Bn=2, curr=1, cap=64, seq=s, sink=None, q=None):
+        return B.gqa_decode_noalloc(hh, Bn, curr, cap, q or t(), t(), t(), t(), seq, sink, None)
+    assert dec(hh=None) == B.GQA_ERR_INVALID_ARG and "plan" in B.gqa_last_error()
+    assert dec(Bn=5) == B.GQA_ERR_CAPACITY and "max_batch" in B.gqa_last_error()
+    assert dec(curr=17) == B.GQA_ERR_CAPACITY
+    assert dec(curr=8, cap=4) == B.GQA_ERR_CAPACITY and "capacity" in B.gqa_last_error()
+    assert dec(seq=None) == B.GQA_ERR_INVALID_ARG and "seqlens_k" in B.gqa_last_error()
+    assert dec(sink=ctypes.c_void_p(FAKE)) == B.GQA_ERR_INVALID_ARG and "use_head_sink" in B.gqa_last_error()
+    assert dec(q=t(ptr=FAKE + 2)) == B.GQA_ERR_UNSUPPORTED and "aligned" in B.gqa_last_error()
+    assert dec(Bn=0) == B.GQA_OK and dec(curr=0) == B.GQA_OK
+    hr = plan(rolling_cache=1, local_window_size=100)
+    assert dec(hh=hr, curr=4, cap=102) == B.GQA_ERR_CAPACITY and "rolling" in B.gqa_last_error()
+
+
 def test_rotary_validation():
     h = plan()
     tab = B.gqa_rotary_tables(FAKE, FAKE, 64)

@@ -62,6 +62,10 @@ def test_decode_and_append_rejections():
         p.decode(q, kc, kc, seq, workspace=torch.zeros(16, dtype=torch.uint8))
     with pytest.raises(ValueError, match="on a GPU"):
         p.decode(q, kc, kc, seq, workspace=torch.zeros(p.workspace_size(), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="on a GPU"):
+        p.decode_noalloc(q, kc, kc, seq)
+    with pytest.raises(TypeError, match="float32"):
+        p.decode_noalloc(q, kc, kc, seq, head_sink=torch.zeros(H, dtype=torch.float16))
     with pytest.raises(ValueError, match="expected"):
         p.append_kv(z(2, HKV, 1, 32), z(2, HKV, 1, 32), kc, kc, seq)
     with pytest.raises(TypeError, match="int32"):

@@ -33,7 +33,7 @@ DTYPE_CODES = {"f32": GQA_F32, "f16": GQA_F16, "bf16": GQA_BF16}
 EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
             "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
-            "gqa_decode_fp8_masked", "gqa_last_error")
+            "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_last_error")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
@@ -123,6 +123,8 @@ def load():
     lib.gqa_decode_fp8.restype = ctypes.c_int
     lib.gqa_decode_fp8_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, F, F, MK, P, S, P]
     lib.gqa_decode_fp8_masked.restype = ctypes.c_int
+    lib.gqa_decode_noalloc.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P]
+    lib.gqa_decode_noalloc.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -162,6 +164,12 @@ def gqa_decode(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, hea
                ws_bytes, stream) -> int:
     return load().gqa_decode(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
                              head_sink, workspace, ws_bytes, stream)
+
+
+def gqa_decode_noalloc(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink,
+                       stream) -> int:
+    return load().gqa_decode_noalloc(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
+                                     head_sink, stream)
 
 
 def gqa_apply_rotary(plan, B, H, L, pos0, x, y, tables, stream) -> int:
@@ -466,6 +474,21 @@ class Plan:
             self._workspace(workspace)
         _same_device(q, k_cache=k_cache, v_cache=v_cache, seqlens_k=seqlens_k, out=out,
                      head_sink=head_sink, workspace=workspace, mask=mask)
+
+    def decode_noalloc(self, q, k_cache, v_cache, seqlens_k, out=None, *, head_sink=None, stream=None):
+        """gqa_decode_noalloc: the decode with the library's static scratch
+        instead of a workspace (no device allocation by the library; out is
+        allocated here when not given)."""
+        import torch
+        self._check_dtype(q, k_cache, v_cache, out)
+        self._decode_args(q, k_cache, v_cache, seqlens_k, out, head_sink, None, None)
+        if out is None:
+            out = torch.empty_like(q)
+        B, _, curr, _ = q.shape
+        check(gqa_decode_noalloc(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_cache),
+                                 tensor_view(v_cache), tensor_view(out), _ptr(seqlens_k), _ptr(head_sink),
+                                 _stream(stream)))
+        return out
 
     @staticmethod
     def _tables(cos, sin):

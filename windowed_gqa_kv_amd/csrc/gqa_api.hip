@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "gqa.h"
@@ -257,10 +258,83 @@ GQA_API gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64
   return hip_status(gqa::launch_append_kv(a, reinterpret_cast<hipStream_t>(hip_stream)), "append_kv launch");
 }
 
+namespace {
+
+// gqa_decode and gqa_decode_noalloc: `scratch_ws` set means the workspace is
+// the library's static scratch array (workspace / ws_bytes are ignored).
+gqa_status decode_impl(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                       gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out, const int32_t* seqlens_k,
+                       const float* head_sink, void* workspace, size_t ws_bytes, void* hip_stream,
+                       bool scratch_ws);
+
+}  // namespace
+
 GQA_API gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
                               gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
                               const int32_t* seqlens_k, const float* head_sink, void* workspace,
                               size_t ws_bytes, void* hip_stream) {
+  return decode_impl(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, workspace,
+                     ws_bytes, hip_stream, false);
+}
+
+GQA_API gqa_status gqa_decode_noalloc(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                                      gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                      const int32_t* seqlens_k, const float* head_sink, void* hip_stream) {
+  return decode_impl(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, nullptr, 0,
+                     hip_stream, true);
+}
+
+// ---------------------------------------------------------------------------
+// The static decode scratch of gqa_decode_noalloc: one array per GPU, held
+// until the process ends.  In host code `scratch` names a host-side stand-in
+// only; kernels get the device address that hipGetSymbolAddress returns for
+// the current device, taken once per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// The arrival counters at the front of a decode workspace must start at zero;
+// every decode leaves them at zero.  A kernel rather than a memset, so that a
+// call under stream capture records an ordinary kernel node.
+__global__ void zero_words(unsigned* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, set up on its first use: the symbol
+// address is looked up and the counters are cleared on `stream`.
+gqa_status scratch_for_current_device(hipStream_t stream, float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GQA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(GQA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_words, dim3(8), dim3(256), 0, stream, reinterpret_cast<unsigned*>(ptr),
+                       gqa::kDecodeMaxTiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "scratch clear launch: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = reinterpret_cast<float*>(g_scratch_ptr[dev]);
+  return GQA_OK;
+}
+
+gqa_status decode_impl(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                       gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out, const int32_t* seqlens_k,
+                       const float* head_sink, void* workspace, size_t ws_bytes, void* hip_stream,
+                       bool scratch_ws) {
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -285,21 +359,34 @@ GQA_API gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t 
   a.head_sink = head_sink;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int dtype = (int)plan->attrs.dtype;
+  const bool softcap = plan->attrs.softcap > 0;
   if (gqa::decode_mfma_supported(dtype, plan->attrs.head_size)) {
     gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
-    const size_t need = geo.ws_floats * sizeof(float);
-    if (workspace == nullptr || ws_bytes < need)
-      return fail(GQA_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
-                  workspace ? "" : ", NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-      return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    float* ws = reinterpret_cast<float*>(workspace);
+    if (scratch_ws) {
+      if (geo.fits) {
+        const size_t need = gqa::decode_mfma_scratch_floats(a, dtype, softcap, geo) * sizeof(float);
+        if (need > kScratchBytes)
+          return fail(GQA_ERR_CAPACITY,
+                      "gqa_decode_noalloc: this call needs %zu bytes of decode scratch, above the static "
+                      "%zu-byte array (use gqa_decode with a workspace)", need, kScratchBytes);
+        if ((st = scratch_for_current_device(stream, &ws)) != GQA_OK) return st;
+      }
+    } else {
+      const size_t need = geo.ws_floats * sizeof(float);
+      if (workspace == nullptr || ws_bytes < need)
+        return fail(GQA_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
+                    workspace ? "" : ", NULL");
+      if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
     if (geo.fits)
-      return hip_status(gqa::launch_decode_mfma(a, dtype, plan->attrs.softcap > 0, geo,
-                                                reinterpret_cast<float*>(workspace), stream),
-                        "decode launch");
+      return hip_status(gqa::launch_decode_mfma(a, dtype, softcap, geo, ws, stream), "decode launch");
   }
   return hip_status(gqa::launch_attn_generic(a, dtype, stream), "decode launch");
 }
+
+}  // namespace
 
 namespace {
 
