@@ -98,75 +98,28 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
-// LDS reads of DMA-filled tiles are inline assembly: the compiler would put a
-// wait for every LDS DMA load in flight (the next tile's) in front of each
-// of them.  Reads are issued and waited for separately, so that the reads of
-// the next batch are in flight while the MFMAs of the current one run; the
-// wait takes the destination registers as read-write operands, so that
-// everything using them is ordered after it.  LDS reads of one wave complete
-// in order, so lgkmcnt(N) leaves exactly the N most recent reads outstanding
-// (no scalar memory operations are issued inside the loop).  Results are
-// consumed whole, as MFMA operands (single elements of a vector-typed
-// inline-asm result are mis-assigned to sub-registers by this compiler); the
-// 64-bit halves of a V operand come back as scalars.
-// Four K operand reads: two k-steps (addresses p0, p1) of both 32-key
-// sub-tiles (immediate offsets OFF and OFF + SUB).
-template <int OFF, int SUB>
-__device__ __forceinline__ void lds_issue_b128x4_at(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3, uint32_t p0,
-                                                    uint32_t p1) {
-  static_assert(OFF >= 0 && OFF + SUB <= 65535, "LDS immediate offset range");
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%6\n\t"
-      "ds_read_b128 %1, %4 offset:%7\n\t"
-      "ds_read_b128 %2, %5 offset:%6\n\t"
-      "ds_read_b128 %3, %5 offset:%7"
-      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
-      : "v"(p0), "v"(p1), "n"(OFF), "n"(OFF + SUB)
-      : "memory");
+// Operand reads of the DMA-filled tiles are ordinary LDS loads, tracked by
+// the compiler: it places the lgkmcnt wait in front of each value's first use
+// and may keep, copy or spill the results like any other value.  All DMA
+// loads are inline assembly, which the compiler does not see as LDS writes,
+// so it puts no wait for them in front of these reads; a tile's DMA is waited
+// for explicitly (wait_vm, then the workgroup barrier) before its stage is
+// read, and the barrier is a compiler memory barrier, so no read moves across
+// it.  The reads are issued one batch ahead of the MFMAs that use them (the
+// source order is the pipeline).
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(const lds_u8* base, uint32_t off) {
+  return *reinterpret_cast<const lds_u32x4*>(base + off + OFF);
 }
-template <int N>
-__device__ __forceinline__ void lds_wait_b128x4(u32x4& a0, u32x4& a1, u32x4& a2, u32x4& a3) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3) : "n"(N) : "memory");
-}
-// Transposing reads of the V operands of one 16-key step: for each 32-wide
-// output block db, rows key0 and key0 + 4 (immediate offsets O0 and O1 from
-// the block's per-lane address).
-template <int O0, int O1>
-__device__ __forceinline__ void lds_issue_tr16x8(uint64_t (&r)[8], const uint32_t (&p)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:%13"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "n"(O0), "n"(O1)
-      : "memory");
-}
-template <int O0, int O1>
-__device__ __forceinline__ void lds_issue_tr16x4(uint64_t (&r)[4], const uint32_t (&p)[2]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
-      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %3, %5 offset:%7"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(p[0]), "v"(p[1]), "n"(O0), "n"(O1)
-      : "memory");
-}
-template <int N>
-__device__ __forceinline__ void lds_wait_tr16(uint64_t (&r)[8]) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
-               : "n"(N)
-               : "memory");
-}
-template <int N>
-__device__ __forceinline__ void lds_wait_tr16(uint64_t (&r)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N) : "memory");
+// One transposing read (ds_read_b64_tr_b16): 4 16-bit values of one column,
+// from the 4 rows whose addresses the lanes of each group of four hold.
+template <int OFF>
+__device__ __forceinline__ uint64_t lds_tr16(const lds_u8* base, uint32_t off) {
+  return __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                          const_cast<lds_i16x4*>(reinterpret_cast<const lds_i16x4*>(base + off + OFF))));
 }
 // One wave-wide LDS DMA load (16 bytes per lane, 1 KB in all) from the
 // uniform base sbase plus this lane's 32-bit byte offset voff, to the LDS
@@ -178,12 +131,19 @@ __device__ __forceinline__ void dma_saddr(const void* sbase, uint32_t voff, uint
   // and knows its value afterwards
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
-// Barrier for waves whose only LDS accesses are the inline-assembly ones:
-// wait for this wave's LDS operations, then meet.  (A fenced barrier would
-// also wait for the next tile's DMA loads, which count as LDS writes.)
+// The same from a per-lane 64-bit address (rows clamped per lane).
+__device__ __forceinline__ void dma_vaddr(const void* addr, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(addr), "{m0}"(lds_addr) : "memory");
+}
+// Barrier between tiles: wait for this wave's LDS operations, then meet.  A
+// fenced barrier would also wait for the next tile's DMA loads, which count as
+// LDS writes; the empty asm statements keep the compiler from moving LDS
+// reads across the barrier instead.
 __device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 // s_waitcnt vmcnt(N) with expcnt and lgkmcnt left unconstrained (gfx9 encoding).
 template <int N>
@@ -213,8 +173,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   __shared__ __attribute__((aligned(16))) uint16_t lds[NSTAGE][2 * TILE];
 
   // ---- work item: XCD-major, KV-head-major, heavy row blocks first ----
-  // A workgroup holds hw query heads of one KV head (hw divides G, at most 8)
-  // and 8 / hw groups of 32 rows of each: all its waves share every K/V tile.
+  // A workgroup holds hw query heads of one KV head (hw divides G, at most 4)
+  // and 4 / hw groups of 32 rows of each: all its waves share every K/V tile.
   const int id = blockIdx.x;
   const int item = (id & 7) * per_xcd + (id >> 3);
   if (item >= items) return;
@@ -308,10 +268,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     } else {
       const int r = RPI * (NDMA * w + i) + lane / CPR, slot = lane % CPR;
       const int j = min(kb + r, kv_hi);
-      __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)j * a.k_ss + 8 * (slot ^ k_swz<D>(r))),
-                                       (lds_void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)j * a.v_ss + 8 * (slot ^ vrow_swz<D>(r))),
-                                       (lds_void*)vdst, 16, 0, 0);
+      dma_vaddr(Kg + (int64_t)j * a.k_ss + 8 * (slot ^ k_swz<D>(r)), (uint32_t)(uintptr_t)(lds_void*)kdst);
+      dma_vaddr(Vg + (int64_t)j * a.v_ss + 8 * (slot ^ vrow_swz<D>(r)), (uint32_t)(uintptr_t)(lds_void*)vdst);
     }
   };
   auto dma_tile = [&](int kb, int buf) {
@@ -371,18 +329,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
   const int kr0 = key_of_m(n);                        // this lane's K row in a sub-tile
 
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0];
+  const lds_u8* const lbase = (const lds_u8*)(lds_void*)&lds[0][0];
   constexpr int kStage = 2 * TILE * 2;  // bytes of one K + V stage
   constexpr int kSubBytes = 2 * 32 * D;  // bytes of one 32-key sub-tile of K
-  // Per-lane LDS addresses of the K operand reads of stage 0, sub-tile 0, one
+  // Per-lane LDS byte offsets of the K operand reads of stage 0, sub-tile 0, one
   // per k-step (chunk 2 ks + h2 of row kr0); the other sub-tile and stage are
   // immediate offsets, since row 32 + r has the same swizzle as row r.
   static_assert(k_swz<D>(32) == k_swz<D>(0) && k_swz<D>(33) == k_swz<D>(1) && k_swz<D>(63) == k_swz<D>(31),
                 "sub-tiles share the K swizzle");
   uint32_t kra[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kra[ks] = lds0 + 2 * kr0 * D + 16 * ((2 * ks + h2) ^ k_swz<D>(kr0));
-  // Per-lane byte offsets (within a stage) of the transposing V reads of
+  for (int ks = 0; ks < KS; ++ks) kra[ks] = 2 * kr0 * D + 16 * ((2 * ks + h2) ^ k_swz<D>(kr0));
+  // Per-lane byte offsets (from the first stage) of the transposing V reads of
   // 16-key step 0: rows 8 (g >> 1) + j (+ 4) of the step, columns
   // 16 (g & 1) + 4 c .. + 3 of each 32-column block.  Step st adds 32 D st
   // bytes and the second row 8 D; the swizzle is the same for all of them.
@@ -396,9 +354,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       vrd[db] = 2 * TILE + 2 * D * key0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
     }
   }
-  uint32_t vra[DB];  // the same as LDS addresses of stage 0; the stage is an immediate offset
-#pragma unroll
-  for (int db = 0; db < DB; ++db) vra[db] = lds0 + vrd[db];
 
   // Sub-tiles (32 keys) of the tile at kb that this wave can see; a tile with
   // at least one is computed whole, and a sub-tile outside every row's band
@@ -408,26 +363,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     a1 = wrows > 0 && kb + 32 <= w_hi && kb + 63 >= w_lo;
   };
 
-  // ---- S^T = K Q^T for both sub-tiles, two k-steps per batch of reads; the
-  // DMA pairs of a later tile ride along, one per batch ----
+  // ---- S^T = K Q^T for both sub-tiles, two k-steps per batch of reads (the
+  // next batch's reads in flight during the current batch's MFMAs); the DMA
+  // pairs of a later tile ride along, one per batch ----
   auto qk = [&](auto st_tag, f32x16 (&sc)[2], auto&& dma_at) {
     constexpr int ST = decltype(st_tag)::value;
     sc[0] = f32x16{};
     sc[1] = f32x16{};
     u32x4 kf[2][4];
     auto issue = [&](int ks, u32x4 (&d)[4]) {
-      lds_issue_b128x4_at<ST * kStage, kSubBytes>(d[0], d[1], d[2], d[3], kra[ks], kra[ks + 1]);
+      d[0] = lds_b128<ST * kStage>(lbase, kra[ks]);
+      d[1] = lds_b128<ST * kStage + kSubBytes>(lbase, kra[ks]);
+      d[2] = lds_b128<ST * kStage>(lbase, kra[ks + 1]);
+      d[3] = lds_b128<ST * kStage + kSubBytes>(lbase, kra[ks + 1]);
     };
     issue(0, kf[0]);
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 2) {
       u32x4 (&cur)[4] = kf[(ks >> 1) & 1];
-      if (ks + 2 < KS) {
-        issue(ks + 2, kf[((ks >> 1) + 1) & 1]);
-        lds_wait_b128x4<4>(cur[0], cur[1], cur[2], cur[3]);
-      } else {
-        lds_wait_b128x4<0>(cur[0], cur[1], cur[2], cur[3]);
-      }
+      if (ks + 2 < KS) issue(ks + 2, kf[((ks >> 1) + 1) & 1]);
       if ((ks >> 1) < NDMA) dma_at(ks >> 1);
       sc[0] = mma32<IS_BF16>(cur[0], qf[ks], sc[0]);
       sc[1] = mma32<IS_BF16>(cur[1], qf[ks], sc[1]);
@@ -530,22 +484,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   auto pv = [&](auto stage_tag, const u32x4 (&pb)[2][2], auto&& before, auto&& after) {
     constexpr int SO = decltype(stage_tag)::value * kStage;
     uint64_t vr[2][2 * DB];
+    // the V operands of 16-key step ST: for each 32-wide output block, rows
+    // key0 and key0 + 4 (immediate offsets from the block's per-lane offset)
     auto vissue = [&](auto st_tag, uint64_t (&d)[2 * DB]) {
-      constexpr int ST = decltype(st_tag)::value;
-      if constexpr (DB == 4)
-        lds_issue_tr16x8<SO + 32 * D * ST, SO + 32 * D * ST + 8 * D>(d, vra);
-      else
-        lds_issue_tr16x4<SO + 32 * D * ST, SO + 32 * D * ST + 8 * D>(d, vra);
+      constexpr int O0 = SO + 32 * D * decltype(st_tag)::value;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        d[2 * db] = lds_tr16<O0>(lbase, vrd[db]);
+        d[2 * db + 1] = lds_tr16<O0 + 8 * D>(lbase, vrd[db]);
+      }
     };
     auto vstep = [&](auto st_tag) {
       constexpr int ST = decltype(st_tag)::value;
       uint64_t (&cur)[2 * DB] = vr[ST & 1];
-      if constexpr (ST + 1 < 4) {
-        vissue(std::integral_constant<int, ST + 1>{}, vr[(ST + 1) & 1]);
-        lds_wait_tr16<2 * DB>(cur);
-      } else {
-        lds_wait_tr16<0>(cur);
-      }
+      if constexpr (ST + 1 < 4) vissue(std::integral_constant<int, ST + 1>{}, vr[(ST + 1) & 1]);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         o[db] = mma32<IS_BF16>(__builtin_bit_cast(u32x4, u64x2{cur[2 * db], cur[2 * db + 1]}),
@@ -647,7 +599,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 template <bool IS_BF16, int D>
 hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
-  // heads per workgroup: the largest power of two that divides G, at most 8
+  // heads per workgroup: the largest power of two that divides G, at most 4 (one per wave)
   const int hw = std::min(a.G & -a.G, kWaves);
   const int rpw = 32 * (kWaves / hw);
   const int nrb = (a.Lq + rpw - 1) / rpw;
