@@ -184,6 +184,25 @@ gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity
                       const int32_t* seqlens_k, const float* head_sink,
                       void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* One decode step in one call: gqa_append_kv of the step's curr new K/V rows
+ * followed by gqa_decode of its curr query rows (the cache as the
+ * concatenation of past and step, "onnx: import GroupQueryAttention decode
+ * steps and its internal rotary", section "What changed"; the rows' positions
+ * and window of "[NPUW] Support GQA sliding-window and smooth-softmax in
+ * DecomposeGQA", section "Sliding window (local_window_size)").  Arguments
+ * as the two calls; the results (out and the cache contents) are those of the
+ * two calls.  On the matrix-core decode (bf16/fp16, head size 64/128/256) it
+ * is one launch: the new rows are copied to their slots while the attention
+ * reads those positions from k_new / v_new directly; otherwise the append
+ * kernel runs first.
+ *   k_new, v_new [B, Hkv, curr, D]; the rest as gqa_decode.
+ * Errors: as gqa_append_kv and gqa_decode. */
+gqa_status gqa_append_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                             gqa_tensor q, gqa_tensor k_new, gqa_tensor v_new,
+                             gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                             const int32_t* seqlens_k, const float* head_sink,
+                             void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* gqa_decode without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation).  The split-KV partials and arrival counters live

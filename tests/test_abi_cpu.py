@@ -154,6 +154,23 @@ def test_decode_validation():
     assert dec(curr=0) == B.GQA_OK
 
 
+def test_append_decode_validation():
+    """gqa_append_decode checks the arguments of both calls it stands for."""
+    h = plan()
+    ws = B.gqa_workspace_size(h)
+    s = ctypes.c_void_p(FAKE)
+    def ad(Bn=2, curr=1, cap=64, seq=s, kn=None, wsb=ws, sink=None):
+        return B.gqa_append_decode(h, Bn, curr, cap, t(), kn or t(), t(), t(), t(), t(), seq, sink,
+                                   ctypes.c_void_p(FAKE), wsb, None)
+    assert ad(curr=17) == B.GQA_ERR_CAPACITY
+    assert ad(curr=8, cap=4) == B.GQA_ERR_CAPACITY and "capacity" in B.gqa_last_error()
+    assert ad(seq=None) == B.GQA_ERR_INVALID_ARG and "seqlens_k" in B.gqa_last_error()
+    assert ad(kn=t(ptr=0)) == B.GQA_ERR_INVALID_ARG and "k_new" in B.gqa_last_error()
+    assert ad(wsb=16) == B.GQA_ERR_INVALID_ARG and "workspace" in B.gqa_last_error()
+    assert ad(sink=ctypes.c_void_p(FAKE)) == B.GQA_ERR_INVALID_ARG
+    assert ad(Bn=0) == B.GQA_OK
+
+
 def test_decode_noalloc_validation():
     """gqa_decode_noalloc checks its arguments like gqa_decode, before it
     looks up its scratch array or launches anything."""

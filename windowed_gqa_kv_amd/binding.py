@@ -33,7 +33,7 @@ DTYPE_CODES = {"f32": GQA_F32, "f16": GQA_F16, "bf16": GQA_BF16}
 EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
             "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
-            "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_last_error")
+            "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_append_decode", "gqa_last_error")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
@@ -125,6 +125,8 @@ def load():
     lib.gqa_decode_fp8_masked.restype = ctypes.c_int
     lib.gqa_decode_noalloc.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P]
     lib.gqa_decode_noalloc.restype = ctypes.c_int
+    lib.gqa_append_decode.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, T, T, P, P, P, S, P]
+    lib.gqa_append_decode.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -170,6 +172,12 @@ def gqa_decode_noalloc(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlen
                        stream) -> int:
     return load().gqa_decode_noalloc(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
                                      head_sink, stream)
+
+
+def gqa_append_decode(plan, B, curr, capacity, q, k_new, v_new, k_cache, v_cache, out, seqlens_k, head_sink,
+                      workspace, ws_bytes, stream) -> int:
+    return load().gqa_append_decode(plan, B, curr, capacity, q, k_new, v_new, k_cache, v_cache, out,
+                                    seqlens_k, head_sink, workspace, ws_bytes, stream)
 
 
 def gqa_apply_rotary(plan, B, H, L, pos0, x, y, tables, stream) -> int:
@@ -474,6 +482,28 @@ class Plan:
             self._workspace(workspace)
         _same_device(q, k_cache=k_cache, v_cache=v_cache, seqlens_k=seqlens_k, out=out,
                      head_sink=head_sink, workspace=workspace, mask=mask)
+
+    def append_decode(self, q, k_new, v_new, k_cache, v_cache, seqlens_k, out=None, *, head_sink=None,
+                      workspace=None, stream=None):
+        """One decode step (gqa_append_decode): append_kv then decode, in one
+        launch on the matrix-core decode."""
+        import torch
+        self._check_dtype(q, k_new, v_new, k_cache, v_cache, out)
+        self._decode_args(q, k_cache, v_cache, seqlens_k, out, head_sink, workspace, None)
+        Bq, curr = self._rows("q", q, self.num_heads)
+        B, curr_n = self._rows("k_new", k_new, self.kv_num_heads)
+        _need((Bq, curr) == (B, curr_n), "q and k_new differ in batch or step length")
+        _need(tuple(v_new.shape) == tuple(k_new.shape), "k_new and v_new differ in shape")
+        _same_device(q, k_new=k_new, v_new=v_new)
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.new_workspace(q.device)
+        check(gqa_append_decode(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_new),
+                                tensor_view(v_new), tensor_view(k_cache), tensor_view(v_cache), tensor_view(out),
+                                _ptr(seqlens_k), _ptr(head_sink), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+        return out
 
     def decode_noalloc(self, q, k_cache, v_cache, seqlens_k, out=None, *, head_sink=None, stream=None):
         """gqa_decode_noalloc: the decode with the library's static scratch

@@ -71,6 +71,15 @@ struct AttnArgs {
   float scale_log2;     // scale * log2(e)
   float scale_over_cap; // scale / softcap (softcap > 0 only)
   float cap_log2;       // softcap * log2(e)
+  // Decode with the step's append fused in (16-bit caches): the curr new K/V
+  // rows of every (batch, KV head) are copied from k_new / v_new to their
+  // cache slots, and the decode reads those positions from k_new / v_new
+  // themselves (no workgroup reads a slot this launch writes).
+  int32_t fuse_append;
+  const void* k_new;
+  const void* v_new;
+  int64_t kn_sb, kn_sh, kn_ss;
+  int64_t vn_sb, vn_sh, vn_ss;
 };
 
 struct BatchSpan {

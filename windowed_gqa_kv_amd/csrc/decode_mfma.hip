@@ -394,8 +394,10 @@ __device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt,
 }
 
 // MASK = 1 / 2: a caller boolean (uint8) / additive (fp32) mask over
-// [B, Hq, curr, capacity], the key index being the cache slot.
-template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8>
+// [B, Hq, curr, capacity], the key index being the cache slot.  FUSE: the
+// step's append is part of the launch (16-bit caches, no mask); a separate
+// instance, so that the other instances keep their code.
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8, bool FUSE = false>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int nrt,
                                                      float* __restrict__ part, unsigned* __restrict__ counters) {
   using RG = Ring<D, KV8>;
@@ -426,6 +428,46 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   const int G = gridDim.x;
   const int k = blockIdx.x;
   const int T = a.B * a.Hkv * nrt;
+
+  // ---- the step's append, fused: new row t of (b, g) into the cache slot of
+  // position total_b - curr + t (mod the ring), with the skip rule of the
+  // append kernel.  Its 16-byte chunks are spread over the whole grid, a few
+  // threads per workgroup.  A thread's first chunk is loaded here and stored
+  // once the split below is known, so no wave waits for the loads.  Nobody
+  // reads these slots in this launch. ----
+  constexpr int kAppendChunks = D / 8;
+  const int ap_items = FUSE ? a.B * a.Hkv * a.Lq * kAppendChunks : 0;
+  u32x4 ap_k = u32x4{}, ap_v = u32x4{};
+  auto ap_coords = [&](int i, int& b, int& g, int& t, int& c) {
+    c = i % kAppendChunks;
+    int r = i / kAppendChunks;
+    t = r % a.Lq;
+    r /= a.Lq;
+    g = r % a.Hkv;
+    b = r / a.Hkv;
+  };
+  auto ap_load = [&](int i, u32x4& kx, u32x4& vx) {
+    int b, g, t, c;
+    ap_coords(i, b, g, t, c);
+    kx = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.k_new) + b * a.kn_sb + g * a.kn_sh +
+                                         (int64_t)t * a.kn_ss + 8 * c);
+    vx = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.v_new) + b * a.vn_sb + g * a.vn_sh +
+                                         (int64_t)t * a.vn_ss + 8 * c);
+  };
+  auto ap_store = [&](int i, const u32x4& kx, const u32x4& vx) {
+    int b, g, t, c;
+    ap_coords(i, b, g, t, c);
+    const int64_t total = (int64_t)a.seqlens[b] + 1;
+    if (total < a.Lq || (!a.ring && total > a.Lk)) return;
+    int64_t slot = total - a.Lq + t;
+    if (a.ring) slot %= a.ring;
+    uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.k));
+    uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.v));
+    *reinterpret_cast<u32x4*>(kc + b * a.k_sb + g * a.k_sh + slot * a.k_ss + 8 * c) = kx;
+    *reinterpret_cast<u32x4*>(vc + b * a.v_sb + g * a.v_sh + slot * a.v_ss + 8 * c) = vx;
+  };
+  if constexpr (FUSE)
+    if (k + G * tid < ap_items) ap_load(k + G * tid, ap_k, ap_v);
 
   // ---- the split of the work (the same in every workgroup) ----
   // Exclusive prefix sum of f(t) over the row tiles into out[0..T].
@@ -533,6 +575,13 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   } else {
     Gs = min(G, U);
   }
+  if constexpr (FUSE) {
+    // the fused append's stores (the loads above have long returned)
+    for (int i = k + G * tid; i < ap_items; i += G * 256) {
+      if (i != k + G * tid) ap_load(i, ap_k, ap_v);
+      ap_store(i, ap_k, ap_v);
+    }
+  }
   if (k >= Gs) return;
   // workgroups first .. first + nvalid - 1 hold the units of (non-empty) tile t
   auto contributors = [&](int t, int& first, int& nvalid) {
@@ -637,6 +686,11 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
 
     const KT* __restrict__ Kg = reinterpret_cast<const KT*>(a.k) + x.b * a.k_sb + x.g * a.k_sh;
     const KT* __restrict__ Vg = reinterpret_cast<const KT*>(a.v) + x.b * a.v_sb + x.g * a.v_sh;
+    // with the append fused in, positions new_lo .. valid - 1 come from the
+    // step's new rows
+    const KT* __restrict__ Kn = reinterpret_cast<const KT*>(a.k_new) + x.b * a.kn_sb + x.g * a.kn_sh;
+    const KT* __restrict__ Vn = reinterpret_cast<const KT*>(a.v_new) + x.b * a.vn_sb + x.g * a.vn_sh;
+    const int new_lo = x.sp.valid - a.Lq;
 
     // Q tile -> LDS by DMA, shared by the 4 waves (instruction i by wave i % 4).
     // Padding rows load the tile's last real row (in bounds, finite); MFMA
@@ -664,7 +718,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     const int turns = a.ring ? c_lo - c_lo % a.ring : 0;
     // Rows past the piece end are clamped to its last key (a real key,
     // finite, masked out for every query row): no per-lane branches.
-    auto issue_t = [&](int s, int j, auto ring_tag) {
+    auto issue_t = [&](int s, int j, auto ring_tag, auto fuse_tag) {
       const int kb = c_lo + kSub * (w + 4 * j);
       unsigned char* kdst = my_ring + s * 2 * RG::kInBytes;
       unsigned char* vdst = kdst + RG::kInBytes;
@@ -676,23 +730,47 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
         const int key = KV8 ? pos / (D / 16) : pos / RG::kSlots;
         const int cc = KV8 ? pos % (D / 16) : (pos % RG::kSlots) ^ swz<D>(key);
         int row = min(kb + key, c_hi);
-        if constexpr (decltype(ring_tag)::value) {
-          row -= turns;
-          row = row >= a.ring ? row - a.ring : row;
+        constexpr int kEl = KV8 ? 16 : 8;  // elements per 16-byte chunk
+        const KT* ks;
+        const KT* vs;
+        if constexpr (decltype(fuse_tag)::value) {
+          // this step's own rows come from k_new / v_new
+          const bool nw_row = row >= new_lo;
+          int slot = row;
+          if constexpr (decltype(ring_tag)::value) {
+            slot -= turns;
+            slot = slot >= a.ring ? slot - a.ring : slot;
+          }
+          ks = nw_row ? Kn + (int64_t)(row - new_lo) * a.kn_ss : Kg + (int64_t)slot * a.k_ss;
+          vs = nw_row ? Vn + (int64_t)(row - new_lo) * a.vn_ss : Vg + (int64_t)slot * a.v_ss;
+        } else {
+          if constexpr (decltype(ring_tag)::value) {
+            row -= turns;
+            row = row >= a.ring ? row - a.ring : row;
+          }
+          ks = Kg + (int64_t)row * a.k_ss;
+          vs = Vg + (int64_t)row * a.v_ss;
         }
         // K/V bytes are read once per call: non-temporal (streaming) loads
-        constexpr int kEl = KV8 ? 16 : 8;  // elements per 16-byte chunk
-        __builtin_amdgcn_global_load_lds((global_void*)(Kg + (int64_t)row * a.k_ss + kEl * cc),
-                                         (lds_void*)(kdst + 1024 * i), 16, 0, kNonTemporal);
-        __builtin_amdgcn_global_load_lds((global_void*)(Vg + (int64_t)row * a.v_ss + kEl * cc),
-                                         (lds_void*)(vdst + 1024 * i), 16, 0, kNonTemporal);
+        __builtin_amdgcn_global_load_lds((global_void*)(ks + kEl * cc), (lds_void*)(kdst + 1024 * i), 16, 0,
+                                         kNonTemporal);
+        __builtin_amdgcn_global_load_lds((global_void*)(vs + kEl * cc), (lds_void*)(vdst + 1024 * i), 16, 0,
+                                         kNonTemporal);
       }
     };
     auto issue = [&](int s, int j) {
-      if (a.ring)
-        issue_t(s, j, std::true_type{});
-      else
-        issue_t(s, j, std::false_type{});
+      if constexpr (FUSE) {
+        if (a.ring)
+          issue_t(s, j, std::true_type{}, std::true_type{});
+        else
+          issue_t(s, j, std::false_type{}, std::true_type{});
+        return;
+      }
+      if (a.ring) {
+        issue_t(s, j, std::true_type{}, std::false_type{});
+      } else {
+        issue_t(s, j, std::false_type{}, std::false_type{});
+      }
     };
     const int npro = min(nw, S);
     for (int j = 0; j < npro; ++j) issue(j, j);
@@ -966,19 +1044,22 @@ int resident_grid(K kernel) {
 
 // The grid of one kernel instance on the current device (computed once per
 // device; a benign race computes the same value).
-template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8>
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8, bool FUSE>
 int grid_of() {
   static int grid_cache[16] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   int G = grid_cache[dev];
-  if (G == 0) G = grid_cache[dev] = resident_grid(decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8>);
+  if (G == 0) G = grid_cache[dev] = resident_grid(decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8, FUSE>);
   return G;
 }
 
 // The instance a call runs on, as compile-time arguments of op.run<...>().
 template <bool IS_BF16, int D, typename Op>
 auto visit_d(const AttnArgs& a, bool softcap, const Op& op) {
+  if (a.fuse_append)  // 16-bit caches, no mask (the host guarantees both)
+    return softcap ? op.template run<IS_BF16, D, true, 0, false, true>()
+                   : op.template run<IS_BF16, D, false, 0, false, true>();
   if (a.kv_fp8) {
     if (a.mask_kind == 1)
       return softcap ? op.template run<IS_BF16, D, true, 1, true>() : op.template run<IS_BF16, D, false, 1, true>();
@@ -1011,20 +1092,20 @@ struct LaunchOp {
   const DecodeGeometry& geo;
   float* ws;
   hipStream_t stream;
-  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8>
+  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8, bool FUSE = false>
   hipError_t run() const {
-    const int G = grid_of<IS_BF16, D, SOFTCAP, MASK, KV8>();
+    const int G = grid_of<IS_BF16, D, SOFTCAP, MASK, KV8, FUSE>();
     unsigned* counters = reinterpret_cast<unsigned*>(ws);
     float* part = ws + geo.counter_floats;
-    hipLaunchKernelGGL((decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8>), dim3(G), dim3(256), 0, stream, a, geo.rows,
-                       geo.row_tiles, part, counters);
+    hipLaunchKernelGGL((decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8, FUSE>), dim3(G), dim3(256), 0, stream, a,
+                       geo.rows, geo.row_tiles, part, counters);
     return hipGetLastError();
   }
 };
 struct GridOp {
-  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8>
+  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8, bool FUSE = false>
   int run() const {
-    return grid_of<IS_BF16, D, SOFTCAP, MASK, KV8>();
+    return grid_of<IS_BF16, D, SOFTCAP, MASK, KV8, FUSE>();
   }
 };
 

@@ -260,12 +260,14 @@ GQA_API gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64
 
 namespace {
 
-// gqa_decode and gqa_decode_noalloc: `scratch_ws` set means the workspace is
-// the library's static scratch array (workspace / ws_bytes are ignored).
+// gqa_decode, gqa_decode_noalloc and gqa_append_decode: `scratch_ws` set
+// means the workspace is the library's static scratch array (workspace /
+// ws_bytes are ignored); `k_new` / `v_new` set means the step's append is
+// part of the call.
 gqa_status decode_impl(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
                        gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out, const int32_t* seqlens_k,
                        const float* head_sink, void* workspace, size_t ws_bytes, void* hip_stream,
-                       bool scratch_ws);
+                       bool scratch_ws, const gqa_tensor* k_new = nullptr, const gqa_tensor* v_new = nullptr);
 
 }  // namespace
 
@@ -282,6 +284,14 @@ GQA_API gqa_status gqa_decode_noalloc(gqa_plan_t plan, int32_t B, int32_t curr, 
                                       const int32_t* seqlens_k, const float* head_sink, void* hip_stream) {
   return decode_impl(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, nullptr, 0,
                      hip_stream, true);
+}
+
+GQA_API gqa_status gqa_append_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                                     gqa_tensor k_new, gqa_tensor v_new, gqa_tensor k_cache, gqa_tensor v_cache,
+                                     gqa_tensor out, const int32_t* seqlens_k, const float* head_sink,
+                                     void* workspace, size_t ws_bytes, void* hip_stream) {
+  return decode_impl(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, workspace,
+                     ws_bytes, hip_stream, false, &k_new, &v_new);
 }
 
 // ---------------------------------------------------------------------------
@@ -331,10 +341,33 @@ gqa_status scratch_for_current_device(hipStream_t stream, float** out) {
   return GQA_OK;
 }
 
+gqa::AppendArgs append_args(const gqa_plan_s* plan, int32_t B, int32_t curr, int64_t capacity,
+                            const gqa_tensor& k_new, const gqa_tensor& v_new, const gqa_tensor& k_cache,
+                            const gqa_tensor& v_cache, const int32_t* seqlens_k) {
+  const int esz = elem_size(plan->attrs.dtype);
+  gqa::AppendArgs a{};
+  a.k_new = k_new.data;
+  a.v_new = v_new.data;
+  a.k_cache = k_cache.data;
+  a.v_cache = v_cache.data;
+  a.kn_sb = k_new.stride_b * esz; a.kn_sh = k_new.stride_h * esz; a.kn_ss = k_new.stride_s * esz;
+  a.vn_sb = v_new.stride_b * esz; a.vn_sh = v_new.stride_h * esz; a.vn_ss = v_new.stride_s * esz;
+  a.kc_sb = k_cache.stride_b * esz; a.kc_sh = k_cache.stride_h * esz; a.kc_ss = k_cache.stride_s * esz;
+  a.vc_sb = v_cache.stride_b * esz; a.vc_sh = v_cache.stride_h * esz; a.vc_ss = v_cache.stride_s * esz;
+  a.seqlens = seqlens_k;
+  a.B = B;
+  a.Hkv = plan->attrs.kv_num_heads;
+  a.curr = curr;
+  a.row_bytes = plan->attrs.head_size * esz;
+  a.capacity = (int32_t)capacity;
+  a.rolling = plan->attrs.rolling_cache;
+  return a;
+}
+
 gqa_status decode_impl(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
                        gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out, const int32_t* seqlens_k,
                        const float* head_sink, void* workspace, size_t ws_bytes, void* hip_stream,
-                       bool scratch_ws) {
+                       bool scratch_ws, const gqa_tensor* k_new, const gqa_tensor* v_new) {
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -354,12 +387,34 @@ gqa_status decode_impl(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacit
   if ((st = check_tensor("k_cache", k_cache, esz)) != GQA_OK) return st;
   if ((st = check_tensor("v_cache", v_cache, esz)) != GQA_OK) return st;
   if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
+  const bool fused = k_new != nullptr;
+  if (fused) {
+    if ((st = check_tensor("k_new", *k_new, esz)) != GQA_OK) return st;
+    if ((st = check_tensor("v_new", *v_new, esz)) != GQA_OK) return st;
+  }
   gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
   a.seqlens = seqlens_k;
   a.head_sink = head_sink;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int dtype = (int)plan->attrs.dtype;
   const bool softcap = plan->attrs.softcap > 0;
+  // The append and the decode in one launch (the matrix-core decode); on the
+  // other path, the append kernel and then the decode.
+  const bool one_launch = fused && gqa::decode_mfma_supported(dtype, plan->attrs.head_size) &&
+                          gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D).fits;
+  if (fused && one_launch) {
+    a.fuse_append = 1;
+    a.k_new = k_new->data;
+    a.v_new = v_new->data;
+    a.kn_sb = k_new->stride_b; a.kn_sh = k_new->stride_h; a.kn_ss = k_new->stride_s;
+    a.vn_sb = v_new->stride_b; a.vn_sh = v_new->stride_h; a.vn_ss = v_new->stride_s;
+  }
+  auto append_first = [&]() -> gqa_status {
+    if (!fused || one_launch) return GQA_OK;
+    return hip_status(gqa::launch_append_kv(append_args(plan, B, curr, capacity, *k_new, *v_new, k_cache, v_cache,
+                                                        seqlens_k), stream),
+                      "append_kv launch");
+  };
   if (gqa::decode_mfma_supported(dtype, plan->attrs.head_size)) {
     gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
     float* ws = reinterpret_cast<float*>(workspace);
@@ -383,6 +438,7 @@ gqa_status decode_impl(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacit
     if (geo.fits)
       return hip_status(gqa::launch_decode_mfma(a, dtype, softcap, geo, ws, stream), "decode launch");
   }
+  if ((st = append_first()) != GQA_OK) return st;
   return hip_status(gqa::launch_attn_generic(a, dtype, stream), "decode launch");
 }
 
