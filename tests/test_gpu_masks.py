@@ -55,6 +55,10 @@ PREFILL = [
     ("bf16", 1, 16, 4, 128, 150, 300, -1, 8.0, True, None, "add", "1h"),       # matrix core, softcap
     ("bf16", 1, 8, 2, 128, 200, 296, 50, 15.0, False, None, "sparse", "11"),   # matrix core, softcap
     ("bf16", 1, 8, 2, 128, 64, 130, -1, 10.0, False, None, "add", "11"),       # streaming, softcap
+    ("bf16", 1, 16, 8, 256, 200, 264, 100, 0.0, True, None, "bool", "1h"),     # matrix core, head size 256
+    ("f16", 2, 8, 4, 256, 130, 256, -1, 30.0, False, (256, 100), "add", "bh"),  # matrix core, 256, softcap
+    ("bf16", 2, 8, 2, 32, 300, 320, 128, 0.0, True, None, "sparse", "11"),    # matrix core, head size 32
+    ("f16", 1, 4, 2, 32, 96, 200, -1, 20.0, False, None, "add", "1h"),        # matrix core, 32, softcap
     ("f32", 1, 4, 2, 32, 64, 64, 16, 0.0, True, None, "bool", "11"),
     ("bf16", 1, 8, 2, 128, 300, 300, -1, 0.0, False, None, "sparse", "11"),
     ("f32", 2, 4, 2, 64, 70, 90, 20, 5.0, False, (90, 33), "add", "b1"),

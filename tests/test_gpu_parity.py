@@ -119,7 +119,8 @@ def test_workload5_large_gqa_prefill_sampled(w5_run, h0):
 # sweeps: tile boundaries, ragged tails, windows, sinks, softcap, layouts
 # --------------------------------------------------------------------------
 PREFILL_SWEEP = []
-for dt, D in (("f32", 32), ("f32", 64), ("bf16", 64), ("bf16", 128), ("f16", 128)):
+for dt, D in (("f32", 32), ("f32", 64), ("bf16", 64), ("bf16", 128), ("f16", 128), ("bf16", 256),
+              ("f16", 32)):
     for (Lq, Lk) in ((64, 64), (200, 200), (37, 300), (300, 130), (129, 129)):
         for W in (1, 2, 3, 63, 64, 65, 127, 128, 129, -1, 100000):
             PREFILL_SWEEP.append((dt, D, Lq, Lk, W))

@@ -115,6 +115,22 @@ def test_large_gqa_prefill_probes(gpu, mode):
     _prefill_probe(w, mode, probe if mode == "mask" else None)
 
 
+@pytest.mark.parametrize("mode", ["mask", "sink", "map"])
+@pytest.mark.parametrize("D", [32, 256])
+def test_prefill_probes_other_head_sizes(gpu, mode, D):
+    """Head sizes 32 and 256 on the matrix-core prefill: a 4096-key prompt
+    with a window, a sink and (head size 32) padded keys."""
+    from windowed_gqa_kv_amd.inputs import Workload
+    if D == 256:
+        w = Workload("probe256", "prefill", "bf16", B=1, Hq=16, Hkv=8, D=256, Lq=4096, Lk=4096, window=1000,
+                     head_sink=True, seed=0)
+    else:
+        w = Workload("probe32", "prefill", "bf16", B=2, Hq=8, Hkv=2, D=32, Lq=4096, Lk=4096, window=700,
+                     head_sink=True, nonpad=(4096, 3000), seed=0)
+    probe = _mask_keys(w.Lk, [0, 1, 63, 64, 699, 700, 999, 1000, 2999, 3000, 3001, 4094, 4095], D, 7 + D)
+    _prefill_probe(w, mode, probe if mode == "mask" else None)
+
+
 def _decode_probe(w, seqlens, mode, probe=None):
     torch.manual_seed(1)
     B, curr, cap = w.B, w.Lq, w.Lk

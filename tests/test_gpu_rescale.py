@@ -154,6 +154,10 @@ PREFILL = [
     ("bursts_bf16_d128_add", "bf16", 128, 768, 768, -1, 0.0, True, None, ("bursts", 6.8, 192, 16), "add"),
     ("stair_bf16_d128_bool_cap", "bf16", 128, 768, 768, 500, 80.0, False, None, ("stair", 7.0, 128), "bool"),
     ("stair_f16_d128_add_cap", "f16", 128, 768, 768, -1, 80.0, False, None, ("stair", 7.0, 128), "add"),
+    ("stair_bf16_d256_win", "bf16", 256, 768, 768, 400, 0.0, True, None, ("stair", 7.5, 64), None),
+    ("bursts_f16_d256_cap_bool", "f16", 256, 768, 768, -1, 80.0, False, None, ("bursts", 6.8, 192, 16), "bool"),
+    ("stair_bf16_d32", "bf16", 32, 768, 768, -1, 0.0, False, None, ("stair", 7.5, 64), None),
+    ("bursts_f16_d32_add", "f16", 32, 768, 768, 500, 0.0, True, None, ("bursts", 6.8, 256, 8), "add"),
 ]
 
 

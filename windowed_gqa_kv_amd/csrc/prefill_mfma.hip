@@ -1,5 +1,5 @@
 // Flash-style prompt attention on CDNA4 matrix cores (bf16 / fp16 inputs,
-// fp32 accumulation), head sizes 64 and 128.
+// fp32 accumulation), head sizes 32, 64, 128 and 256.
 //
 // What it computes is the definition in include/gqa.h; the method is the
 // streaming path of "Attention Kernel Design" (section "Compute paths": visit
@@ -17,7 +17,8 @@
 //     same keys, so K and V tiles of 64 rows are loaded once per workgroup:
 //     from global memory straight into LDS by LDS DMA (global_load_lds_dwordx4,
 //     no registers held by loads in flight), double buffered, one barrier per
-//     tile.  Two workgroups fit on a CU.
+//     tile.  Two workgroups fit on a CU (one at head size 256, whose tiles
+//     take 128 KB of LDS and whose waves use up to 512 registers).
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q held in
 //     registers for the whole kernel), so each lane ends up owning one query
 //     row and 16 keys of every 32-key sub-tile.  The K rows fed to the MFMA M
@@ -79,19 +80,23 @@ __device__ __forceinline__ int key_of_m(int m) {
 // touches per 16 lanes land on 16 different bank groups.
 template <int D>
 __host__ __device__ constexpr int k_swz(int r) {
-  if constexpr (D == 128)
-    return r & 15;
-  else
+  if constexpr (D >= 128)
+    return r & 15;  // 16 (or 32) chunks per row
+  else if constexpr (D == 64)
     return (r >> 1) & 7;
+  else
+    return (r >> 2) & 3;  // 4 chunks per row: rows r and r + 4 share banks
 }
 // V tile rows (row-major, 16-byte chunks XOR-swizzled by key): the
 // transposing reads of the P*V operand then hit every bank equally.
 template <int D>
 __host__ __device__ constexpr int vrow_swz(int key) {
-  if constexpr (D == 128)
+  if constexpr (D >= 128)
     return 4 * (key & 3);
-  else
+  else if constexpr (D == 64)
     return 4 * ((key >> 1) & 1);
+  else
+    return 0;  // one 32-column block: the four rows of a read are 256 contiguous bytes
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -160,11 +165,12 @@ typedef __attribute__((address_space(1))) const unsigned char global_u8;
 typedef __attribute__((address_space(1))) const f32x4 global_f32x4;
 typedef __attribute__((address_space(1))) const float global_f32;
 
-// Two waves per SIMD (two workgroups per CU): the register budget is 256.
+// Two waves per SIMD (two workgroups per CU): the register budget is 256;
+// at head size 256 one wave per SIMD with up to 512.
 // MASK = 1: a caller boolean mask (uint8, nonzero attends) over [B, Hq, Lq, Lk];
 // MASK = 2: a caller additive mask (fp32, added to the scaled logit).
 template <bool IS_BF16, int D, bool SOFTCAP, int MASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void prefill_mfma_kernel(
     AttnArgs a, int nrb, int items, int per_xcd, int hw) {
   constexpr int KS = D / 16;    // k-steps of the QK^T contraction
   constexpr int DB = D / 32;    // 32-wide output blocks
@@ -624,7 +630,8 @@ hipError_t launch_t(const AttnArgs& a, bool softcap, hipStream_t stream) {
 }  // namespace
 
 bool prefill_mfma_supported(int dtype, int head_size) {
-  return (dtype == kBF16 || dtype == kF16) && (head_size == 64 || head_size == 128);
+  return (dtype == kBF16 || dtype == kF16) &&
+         (head_size == 32 || head_size == 64 || head_size == 128 || head_size == 256);
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, int dtype, bool softcap, hipStream_t stream) {
@@ -632,9 +639,13 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, int dtype, bool softcap, hipSt
   if (dtype == kBF16) {
     if (a.D == 128) return launch_t<true, 128>(a, softcap, stream);
     if (a.D == 64) return launch_t<true, 64>(a, softcap, stream);
+    if (a.D == 256) return launch_t<true, 256>(a, softcap, stream);
+    if (a.D == 32) return launch_t<true, 32>(a, softcap, stream);
   } else if (dtype == kF16) {
     if (a.D == 128) return launch_t<false, 128>(a, softcap, stream);
     if (a.D == 64) return launch_t<false, 64>(a, softcap, stream);
+    if (a.D == 256) return launch_t<false, 256>(a, softcap, stream);
+    if (a.D == 32) return launch_t<false, 32>(a, softcap, stream);
   }
   return hipErrorInvalidValue;
 }
