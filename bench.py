@@ -2,9 +2,10 @@
 
 Default workload: single-token decode, bf16, B=8, Hq=32, Hkv=8, D=128, KV
 capacity 4096, seqlens_k ~ integers[1024, 4096), smooth_softmax (zero sink),
-window off.  One step = the whole decode path for one batch: gqa_append_kv
-(the new token's K/V into the cache) then gqa_decode (split-KV attention and
-the merge of the splits, one kernel).  Inputs are resident in HBM before
+window off.  One step = the whole decode path for one batch:
+gqa_append_decode, one launch that puts the new token's K/V into the cache
+and runs the split-KV attention with the merge of the splits (the same step
+as two launches, gqa_append_kv then gqa_decode, is timed beside it).  Inputs are resident in HBM before
 timing starts.  Every step works on a different replica of the KV cache (R
 replicas, >= 1 GiB in total), so a step cannot be served from the 256 MB
 Infinity Cache left warm by the previous one.
@@ -14,10 +15,11 @@ the kept key range, Q, O, and the appended rows) / wall time per step, the
 steps being replayed from HIP graphs that hold one step per cache replica in
 turn (captured once, as consecutive layers of a serving loop would run);
 the eager per-step time is reported too.
-`roofline` is for the dominant kernel (gqa_decode): its average duration is
-timed with HIP events on the stream it runs on, around graphs of back-to-back
-decode launches (one per cache replica); events around each eager launch,
-which also count its dispatch latency, are reported beside it.  `cpu_baseline` times the float64 oracle on
+`roofline` is for the dominant kernel (the step's one launch): its average
+duration is timed with HIP events on the stream it runs on, around graphs of
+back-to-back launches (one per cache replica); events around each eager
+launch, which also count its dispatch latency, are reported beside it, and so
+is the decode kernel alone (gqa_decode).  `cpu_baseline` times the float64 oracle on
 this host (the oracle as it stands, on a bounded number of full decode
 steps).  `extra` reports the prompt workloads (TFLOP/s against the bf16 MFMA
 peak) and the speculative-decode workload the same way; `rotary` times the
@@ -119,16 +121,22 @@ def bench_decode(w, steps, warmup, replicas):
     ws = torch.zeros(max(16, plan.workspace_size()), dtype=torch.uint8, device="cuda")
 
     def step(i, ev=None):
+        # one decode step: the new token's K/V into the cache and the
+        # attention, one launch (gqa_append_decode)
         kc, vc = caches[i % R]
-        plan.append_kv(kn, vn, kc, vc, seq)
         if ev is not None:
             ev[0].record()
-        plan.decode(q, kc, vc, seq, out, head_sink=sink, workspace=ws)
+        plan.append_decode(q, kn, vn, kc, vc, seq, out, head_sink=sink, workspace=ws)
         if ev is not None:
             ev[1].record()
 
-    # Eager steps: warm-up, then the decode kernel timed with HIP events on
-    # the stream it is launched on (the roofline figure).
+    def step_two_launches(i):
+        kc, vc = caches[i % R]
+        plan.append_kv(kn, vn, kc, vc, seq)
+        plan.decode(q, kc, vc, seq, out, head_sink=sink, workspace=ws)
+
+    # Eager steps: warm-up, then each launch timed with HIP events on the
+    # stream it runs on (dispatch latency included).
     for i in range(warmup):
         step(i)
     evs = _events(steps)
@@ -138,60 +146,73 @@ def bench_decode(w, steps, warmup, replicas):
         step(warmup + i, evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    step_ms_events_each = sum(a.elapsed_time(b) for a, b in evs) / steps
     eager_ms = (t1 - t0) * 1000.0 / steps
 
     # The step as a serving loop runs it, from HIP graphs: one graph holds R
-    # consecutive steps (append_kv then decode on every cache replica in
-    # turn, as consecutive layers would run), another one step per replica;
-    # K steps are floor(K / R) replays of the first and K mod R of the
-    # second, so the host's per-launch work is out of the step.
-    chain = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(chain):
+    # consecutive steps (one per cache replica, as consecutive layers would
+    # run), another one step per replica; K steps are floor(K / R) replays of
+    # the first and K mod R of the second, so the host's per-launch work is
+    # out of the step.
+    def graphs_of(fn):
+        chain = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(chain):
+            for r in range(R):
+                fn(r)
+        single = []
         for r in range(R):
-            step(r)
-    single = []
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(r)
-        single.append(g)
-    for i in range(max(1, warmup // R)):
-        chain.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps // R):
-        chain.replay()
-    for i in range(steps % R):
-        single[i].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1000.0 / steps
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(r)
+            single.append(g)
+        return chain, single
+
+    def time_steps(chain, single):
+        for i in range(max(1, warmup // R)):
+            chain.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps // R):
+            chain.replay()
+        for i in range(steps % R):
+            single[i].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1000.0 / steps
+
+    chain, single = graphs_of(step)
+    ms = time_steps(chain, single)
+    del chain, single
+    chain, single = graphs_of(step_two_launches)
+    ms_two = time_steps(chain, single)
     del chain, single
 
-    # The decode kernel's average duration for the roofline: decode launches
-    # back to back (one per replica, from a graph), between two HIP events on
-    # the stream they run on.
-    dchain = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(dchain):
-        for r in range(R):
-            plan.decode(q, caches[r][0], caches[r][1], seq, out, head_sink=sink, workspace=ws)
-    dchain.replay()
-    nrep = max(1, steps // R)
-    e0, e1 = _events(1)[0]
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(nrep):
-        dchain.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    dec_b2b_ms = e0.elapsed_time(e1) / (nrep * R)
-    del dchain
+    # Average kernel durations for the roofline: launches back to back (one
+    # per replica, from a graph), between two HIP events on the stream they
+    # run on -- the fused step's kernel, and the decode alone.
+    def b2b(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(R):
+                fn(r)
+        g.replay()
+        nrep = max(1, steps // R)
+        e0, e1 = _events(1)[0]
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(nrep):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (nrep * R)
+
+    fused_ms = b2b(step)
+    dec_ms = b2b(lambda r: plan.decode(q, caches[r][0], caches[r][1], seq, out, head_sink=sink, workspace=ws))
     s = d["seqlens_k"].numpy()
     dec_bytes = work.decode_bytes(s, w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window)
     app_bytes = work.append_bytes(w.B, w.Hkv, w.Lq, w.D, w.dtype)
-    return dict(ms_per_step=ms, eager_ms_per_step=eager_ms, step_bytes=dec_bytes + app_bytes, kernel_ms=dec_b2b_ms,
-                kernel_ms_events_each=dec_ms, kernel_bytes=dec_bytes, replicas=R, inputs=d)
+    return dict(ms_per_step=ms, two_launch_ms_per_step=ms_two, eager_ms_per_step=eager_ms,
+                step_bytes=dec_bytes + app_bytes, kernel_ms=fused_ms, kernel_ms_events_each=step_ms_events_each,
+                decode_only_ms=dec_ms, decode_bytes=dec_bytes, replicas=R, inputs=d)
 
 
 def bench_prefill(w, steps, warmup):
@@ -551,7 +572,8 @@ def main():
 
     r = bench_decode(w, args.steps, args.warmup, args.replicas)
     value = r["step_bytes"] / (r["ms_per_step"] / 1e3) / 1e9
-    achieved = r["kernel_bytes"] / (r["kernel_ms"] / 1e3) / 1e9
+    achieved = r["step_bytes"] / (r["kernel_ms"] / 1e3) / 1e9
+    dec_only = r["decode_bytes"] / (r["decode_only_ms"] / 1e3) / 1e9
     dec_src = ["decode_mfma.hip", "common.h", "kernels.h"]
     line = {
         "metric": METRIC,
@@ -567,19 +589,27 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1); KV cache rotated over "
                 f"{r['replicas']} replicas so no step reads a warm Infinity Cache)",
-        "step": f"append_kv + decode; timed from HIP graphs of {r['replicas']} consecutive steps (one per "
-                f"cache replica); eager launches take {r['eager_ms_per_step'] * 1e3:.1f} us per step",
+        "step": f"gqa_append_decode (the new token's K/V into the cache and the attention, one launch); "
+                f"timed from HIP graphs of {r['replicas']} consecutive steps (one per cache replica); "
+                f"eager launches take {r['eager_ms_per_step'] * 1e3:.1f} us per step; as two launches "
+                f"(gqa_append_kv, gqa_decode) a step takes {r['two_launch_ms_per_step'] * 1e3:.1f} us",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "curr": w.Lq, "kv_capacity": w.Lk, "window": w.window,
                    "seqlens_k": [int(x) for x in r["inputs"]["seqlens_k"].numpy()],
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel (gqa_decode: split-KV stream with fused combine)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_kernel (gqa_append_decode: the step's append, the split-KV stream and "
+                               "the fused combine)",
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": _traffic("decode", w.name, dec_src),
-                     "kernel_ms": round(r["kernel_ms"], 5), "bytes_per_launch": r["kernel_bytes"],
-                     "timing": f"HIP events around {r['replicas']}-launch graphs of back-to-back decodes; "
-                               f"events around each eager launch read {r['kernel_ms_events_each'] * 1e3:.1f} us"},
+                     "traffic": _traffic("append_decode", w.name, dec_src),
+                     "kernel_ms": round(r["kernel_ms"], 5), "bytes_per_launch": r["step_bytes"],
+                     "timing": f"HIP events around {r['replicas']}-launch graphs of back-to-back launches; "
+                               f"events around each eager launch read {r['kernel_ms_events_each'] * 1e3:.1f} us",
+                     "decode_only": {"kernel": "decode_kernel (gqa_decode)", "kernel_ms": round(r["decode_only_ms"], 5),
+                                     "bytes_per_launch": r["decode_bytes"], "achieved": round(dec_only, 2),
+                                     "frac": round(dec_only / PEAK_HBM_GBS, 4),
+                                     "traffic": _traffic("decode", w.name, dec_src)}},
     }
 
     if not args.no_extra:
@@ -587,13 +617,19 @@ def main():
         for wid in (4,):
             w4 = WORKLOADS[wid]
             r4 = bench_decode(w4, args.extra_steps, 3, 0)
-            a4 = r4["kernel_bytes"] / (r4["kernel_ms"] / 1e3) / 1e9
+            a4 = r4["step_bytes"] / (r4["kernel_ms"] / 1e3) / 1e9
+            d4 = r4["decode_bytes"] / (r4["decode_only_ms"] / 1e3) / 1e9
             extra.append({"workload": w4.name, "value": round(r4["step_bytes"] / (r4["ms_per_step"] / 1e3) / 1e9, 2),
                           "unit": "GB/s", "ms_per_step": round(r4["ms_per_step"], 5),
+                          "two_launch_ms_per_step": round(r4["two_launch_ms_per_step"], 5),
                           "eager_ms_per_step": round(r4["eager_ms_per_step"], 5),
-                          "roofline": {"bound": "hbm", "achieved": round(a4, 2), "peak": PEAK_HBM_GBS,
+                          "roofline": {"bound": "hbm", "kernel": "decode_kernel (gqa_append_decode)",
+                                       "achieved": round(a4, 2), "peak": PEAK_HBM_GBS,
                                        "unit": "GB/s", "frac": round(a4 / PEAK_HBM_GBS, 4),
-                                       "kernel_ms": round(r4["kernel_ms"], 5)}})
+                                       "kernel_ms": round(r4["kernel_ms"], 5),
+                                       "decode_only": {"kernel_ms": round(r4["decode_only_ms"], 5),
+                                                       "achieved": round(d4, 2),
+                                                       "frac": round(d4 / PEAK_HBM_GBS, 4)}}})
             del r4
         for wid in (3, 5):
             wp = WORKLOADS[wid]
