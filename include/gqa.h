@@ -249,6 +249,23 @@ gqa_status gqa_apply_rotary(gqa_plan_t plan, int32_t B, int32_t H, int32_t L, in
                             gqa_tensor x, gqa_tensor y, const gqa_rotary_tables* tables,
                             void* hip_stream);
 
+/* gqa_prefill with the rotary embedding of Q fused into the prefill's load
+ * of Q (do_rotary of the page above: a prompt's rows take positions 0 .. S-1,
+ * bottom-right aligned): query row i is turned at position Lk - Lq + i
+ * exactly as gqa_apply_rotary would turn it (fp32, then RNE to the plan's
+ * type), and the result equals gqa_apply_rotary on q followed by
+ * gqa_prefill, bit for bit.  K arrives turned (gqa_apply_rotary with pos0 =
+ * 0, or a cache filled by gqa_append_kv_rotary); V is not turned.
+ * Arguments as gqa_prefill; tables as gqa_apply_rotary, covering positions
+ * 0 .. Lk - 1.  Needs a bf16 or fp16 plan of head size 32, 64, 128 or 256
+ * (the matrix-core prefill).
+ * Errors: as gqa_prefill; CAPACITY when tables->max_pos < Lk; UNSUPPORTED for
+ *   other plans and for K/V row strides of 2^24 elements or more. */
+gqa_status gqa_prefill_rotary(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk,
+                              gqa_tensor q, gqa_tensor k, gqa_tensor v, gqa_tensor out,
+                              const int64_t* nonpad_kv_seqlen, const float* head_sink,
+                              const gqa_rotary_tables* tables, void* hip_stream);
+
 /* gqa_append_kv with rotary, in one launch: the curr new K rows are turned at
  * their positions before they enter the cache (K is cached rotated, the page
  * above), the new V rows are copied, and the curr query rows are turned into

@@ -213,6 +213,14 @@ def test_rotary_validation():
     assert rot(x=t(ptr=FAKE + 2)) == B.GQA_ERR_UNSUPPORTED and "aligned" in B.gqa_last_error()
     assert rot(tables=B.gqa_rotary_tables(FAKE, FAKE, 0)) == B.GQA_ERR_INVALID_ARG
     assert rot(L=0) == B.GQA_OK and rot(H=0) == B.GQA_OK
+    # prefill with Q turned inside: the tables cover positions 0 .. Lk - 1
+    def pr(Lk=8, tables=tab, hh=h, Bn=2):
+        return B.gqa_prefill_rotary(hh, Bn, 8, Lk, t(), t(), t(), t(), None, None, tables, None)
+    assert pr(tables=None) == B.GQA_ERR_INVALID_ARG and "tables" in B.gqa_last_error()
+    assert pr(Lk=65) == B.GQA_ERR_CAPACITY and "rotary tables" in B.gqa_last_error()
+    st, hf = B.gqa_plan(attrs(dtype=B.GQA_F32), 4, 16, 1024)
+    assert pr(hh=hf) == B.GQA_ERR_UNSUPPORTED and "gqa_apply_rotary" in B.gqa_last_error()
+    assert pr(Bn=0) == B.GQA_OK
 
 
 def test_rolling_cache_validation():

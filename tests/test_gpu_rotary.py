@@ -181,3 +181,51 @@ def test_rotary_full_size_long_prompt_sampled(gpu):
         before = x[..., :h] ** 2 + x[..., h:] ** 2
         after = y[..., :h] ** 2 + y[..., h:] ** 2
         assert float(((after - before).abs() / (before + 1e-6)).max()) < 2 * 2.0 ** -7
+
+
+@pytest.mark.parametrize("dtype,D,Lq,Lk,W,sink,nonpad", [
+    ("bf16", 128, 200, 260, 64, True, None),      # bottom-right: rows at positions 60 .. 259
+    ("f16", 64, 300, 300, -1, False, (300, 150)),
+    ("bf16", 256, 130, 130, 100, True, None),
+    ("bf16", 32, 97, 400, -1, False, None),
+])
+def test_prefill_rotary_equals_apply_rotary_then_prefill(gpu, dtype, D, Lq, Lk, W, sink, nonpad):
+    """gqa_prefill_rotary (Q turned while the prefill loads it) against
+    gqa_apply_rotary on Q followed by gqa_prefill: bitwise equal; and against
+    the oracle's rotary + attention within the tolerances."""
+    B = 1 if nonpad is None else len(nonpad)
+    w = Workload("rotfused", "prefill", dtype, B=B, Hq=8, Hkv=2, D=D, Lq=Lq, Lk=Lk, window=W,
+                 head_sink=sink, nonpad=nonpad, value_scale=0.5, seed=95 + D + Lq)
+    d = generate(w)
+    cos, sin = rotary_tables(Lk, D)
+    plan = make_plan(w)
+    cs, sn = cos.cuda(), sin.cuda()
+    np_d = None if d["nonpad"] is None else d["nonpad"].cuda()
+    sk = None if d["head_sink"] is None else d["head_sink"].cuda()
+    k_r = plan.apply_rotary(d["k"].cuda(), 0, cs, sn)
+    q_r = plan.apply_rotary(d["q"].cuda(), Lk - Lq, cs, sn)
+    want_gpu = plan.prefill(q_r, k_r, d["v"].cuda(), nonpad_kv_seqlen=np_d, head_sink=sk)
+    got = plan.prefill_rotary(d["q"].cuda(), k_r, d["v"].cuda(), cs, sn, nonpad_kv_seqlen=np_d, head_sink=sk)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want_gpu), "fused rotary differs from apply_rotary + prefill"
+    qo, ko = oracle.rotary.rotate_prefill(to_f64(d["q"]), to_f64(d["k"]), to_f64(cos), to_f64(sin))
+    want = oracle.prefill(_round(qo, dtype), _round(ko, dtype), to_f64(d["v"]), scale=w.sm_scale, window=W,
+                          head_sink=to_f64(d["head_sink"]),
+                          nonpad_kv_seqlen=None if d["nonpad"] is None else d["nonpad"].numpy())
+    compare(got, want, dtype, f"prefill_rotary {dtype} D={D}")
+
+
+def test_prefill_rotary_full_size_long_prompt(gpu):
+    """The long prompt (32 x 8192 rows, window 4096) with Q turned inside the
+    prefill: bitwise equal to the two-pass path."""
+    from windowed_gqa_kv_amd.inputs import WORKLOADS
+    w = WORKLOADS[3]
+    d = generate(w)
+    cos, sin = (t.cuda() for t in rotary_tables(w.Lk, w.D))
+    plan = make_plan(w)
+    k_r = plan.apply_rotary(d["k"].cuda(), 0, cos, sin)
+    q = d["q"].cuda()
+    a = plan.prefill(plan.apply_rotary(q, 0, cos, sin), k_r, d["v"].cuda())
+    b = plan.prefill_rotary(q, k_r, d["v"].cuda(), cos, sin)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -33,7 +33,8 @@ DTYPE_CODES = {"f32": GQA_F32, "f16": GQA_F16, "bf16": GQA_BF16}
 EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
             "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
-            "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_append_decode", "gqa_last_error")
+            "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_append_decode", "gqa_prefill_rotary",
+            "gqa_last_error")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
@@ -127,6 +128,8 @@ def load():
     lib.gqa_decode_noalloc.restype = ctypes.c_int
     lib.gqa_append_decode.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, T, T, P, P, P, S, P]
     lib.gqa_append_decode.restype = ctypes.c_int
+    lib.gqa_prefill_rotary.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, RT, P]
+    lib.gqa_prefill_rotary.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
     lib.gqa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -183,6 +186,11 @@ def gqa_append_decode(plan, B, curr, capacity, q, k_new, v_new, k_cache, v_cache
 def gqa_apply_rotary(plan, B, H, L, pos0, x, y, tables, stream) -> int:
     return load().gqa_apply_rotary(plan, B, H, L, pos0, x, y,
                                    None if tables is None else ctypes.byref(tables), stream)
+
+
+def gqa_prefill_rotary(plan, B, Lq, Lk, q, k, v, out, nonpad_kv_seqlen, head_sink, tables, stream) -> int:
+    return load().gqa_prefill_rotary(plan, B, Lq, Lk, q, k, v, out, nonpad_kv_seqlen, head_sink,
+                                     None if tables is None else ctypes.byref(tables), stream)
 
 
 def gqa_append_kv_rotary(plan, B, curr, capacity, q, q_rot, k_new, v_new, k_cache, v_cache,
@@ -544,6 +552,29 @@ class Plan:
         B, H, L, _ = x.shape
         check(gqa_apply_rotary(self._h, B, H, L, pos0, tensor_view(x), tensor_view(out),
                                self._tables(cos, sin), _stream(stream)))
+        return out
+
+    def prefill_rotary(self, q, k, v, cos, sin, out=None, *, nonpad_kv_seqlen=None, head_sink=None, stream=None):
+        """gqa_prefill_rotary: q [B, Hq, Lq, D] not yet turned (turned in the
+        prefill at positions Lk - Lq + i), k [B, Hkv, Lk, D] already turned."""
+        import torch
+        self._check_dtype(q, k, v, out)
+        B, Lq = self._rows("q", q, self.num_heads)
+        Bk, Lk = self._rows("k", k, self.kv_num_heads)
+        _need(tuple(v.shape) == tuple(k.shape), "k and v differ in shape")
+        _need(Bk == B, f"q has {B} batches, k has {Bk}")
+        _need(out is None or tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+        _aux("nonpad_kv_seqlen", nonpad_kv_seqlen, torch.int64, B)
+        _aux("head_sink", head_sink, torch.float32, self.num_heads)
+        if cos.shape[1] * 2 != self.head_size:
+            raise ValueError("rotary tables need head_size / 2 columns")
+        _same_device(q, k=k, v=v, out=out, nonpad_kv_seqlen=nonpad_kv_seqlen, head_sink=head_sink,
+                     cos=cos, sin=sin)
+        if out is None:
+            out = torch.empty_like(q)
+        check(gqa_prefill_rotary(self._h, B, Lq, Lk, tensor_view(q), tensor_view(k), tensor_view(v),
+                                 tensor_view(out), _ptr(nonpad_kv_seqlen), _ptr(head_sink),
+                                 self._tables(cos, sin), _stream(stream)))
         return out
 
     def append_kv_rotary(self, q, k_new, v_new, k_cache, v_cache, seqlens_k, cos, sin,

@@ -80,6 +80,11 @@ struct AttnArgs {
   const void* v_new;
   int64_t kn_sb, kn_sh, kn_ss;
   int64_t vn_sb, vn_sh, vn_ss;
+  // Prompt with rotary on Q (prefill only): when set, query row i is turned
+  // at its position q_offset + i with these fp32 [positions, D/2] tables as
+  // it is loaded (K arrives turned).
+  const float* rot_cos;
+  const float* rot_sin;
 };
 
 struct BatchSpan {
@@ -167,6 +172,15 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
   else
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+
+// The rotary turn of one pair (a, b) = (element i, element i + D/2) by the
+// angle with cosine c and sine s: (a c - b s, b c + a s), in fp32 with the
+// products contracted the same way wherever it is computed (so a turn done
+// while loading equals the rotary kernel's bit for bit).
+__device__ __forceinline__ void rot_pair(float a, float b, float c, float s, float& u, float& w) {
+  u = fmaf(a, c, -(b * s));
+  w = fmaf(b, c, a * s);
 }
 
 // ---------------------------------------------------------------------------

@@ -499,6 +499,46 @@ GQA_API gqa_status gqa_apply_rotary(gqa_plan_t plan, int32_t B, int32_t H, int32
                     "rotary launch");
 }
 
+GQA_API gqa_status gqa_prefill_rotary(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk, gqa_tensor q,
+                                      gqa_tensor k, gqa_tensor v, gqa_tensor out,
+                                      const int64_t* nonpad_kv_seqlen, const float* head_sink,
+                                      const gqa_rotary_tables* tables, void* hip_stream) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || Lq < 0 || Lk < 0) return fail(GQA_ERR_INVALID_ARG, "B, Lq and Lk must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (Lq > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "Lq = %d exceeds the plan's max_q_len %d", Lq, plan->max_q_len);
+  if (Lk > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "Lk = %lld exceeds the plan's max_kv_len %lld", (long long)Lk,
+                (long long)plan->max_kv_len);
+  gqa_status st = check_sink(plan, head_sink);
+  if (st != GQA_OK) return st;
+  // query row i sits at position Lk - Lq + i, at most Lk - 1
+  if ((st = check_tables(tables, Lk)) != GQA_OK) return st;
+  const int dtype = (int)plan->attrs.dtype;
+  if (!gqa::prefill_mfma_supported(dtype, plan->attrs.head_size))
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_rotary needs a bf16 or fp16 plan of head size 32, 64, 128 or "
+                "256 (otherwise call gqa_apply_rotary, then gqa_prefill)");
+  if (B == 0 || Lq == 0) return GQA_OK;
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("q", q, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
+  if (Lk > 0) {
+    if ((st = check_tensor("k", k, esz)) != GQA_OK) return st;
+    if ((st = check_tensor("v", v, esz)) != GQA_OK) return st;
+  }
+  gqa::AttnArgs a = make_args(plan, q, k, v, out, B, Lq, Lk, 0);
+  if (a.k_ss >= (int64_t(1) << 24) || a.v_ss >= (int64_t(1) << 24))
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_rotary: K/V row strides of 2^24 elements or more");
+  a.nonpad = nonpad_kv_seqlen;
+  a.head_sink = head_sink;
+  a.rot_cos = tables->cos;
+  a.rot_sin = tables->sin;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  if (Lk == 0) return hip_status(gqa::launch_attn_generic(a, dtype, stream), "prefill launch");  // zeros
+  return hip_status(gqa::launch_prefill_mfma(a, dtype, plan->attrs.softcap > 0, stream), "prefill_rotary launch");
+}
+
 GQA_API gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
                                         gqa_tensor q, gqa_tensor q_rot, gqa_tensor k_new, gqa_tensor v_new,
                                         gqa_tensor k_cache, gqa_tensor v_cache, const int32_t* seqlens_k,

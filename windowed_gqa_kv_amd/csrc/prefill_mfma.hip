@@ -226,6 +226,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
 
   // Q rows stay in registers (B operand of S^T = K Q^T).
   u32x4 qf[KS];
+  const bool rot = a.rot_cos != nullptr;
+  f32x4 rc[KS / 2][2], rs[KS / 2][2];  // rotary angles of the row (cos, sin), when rot
   {
     const bool ok = my_row < a.Lq;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh +
@@ -235,8 +237,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
       u32x4 z = {0u, 0u, 0u, 0u};
       qf[ks] = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : z;
     }
+    // Rotary on Q: the lane's elements i of k-step ks < KS/2 and their
+    // partners i + D/2 of k-step ks + KS/2 turn by the angles of the row's
+    // position (the rotary kernel's arithmetic, then RNE to the input type).
+    // The angles are loaded with Q; the turn waits until the first tile's
+    // DMA is on its way.
+    if (rot && ok && my_p >= 0) {
+      const float* cr = a.rot_cos + (int64_t)my_p * (D / 2) + 8 * h2;
+      const float* sr = a.rot_sin + (int64_t)my_p * (D / 2) + 8 * h2;
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks) {
+        rc[ks][0] = *reinterpret_cast<const f32x4*>(cr + 16 * ks);
+        rc[ks][1] = *reinterpret_cast<const f32x4*>(cr + 16 * ks + 4);
+        rs[ks][0] = *reinterpret_cast<const f32x4*>(sr + 16 * ks);
+        rs[ks][1] = *reinterpret_cast<const f32x4*>(sr + 16 * ks + 4);
+      }
+    }
   }
-
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
@@ -528,6 +545,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
     if (nblk > 0) mask_load(kv_lo, mk_nxt);
   __builtin_amdgcn_s_waitcnt(0);  // Q registers, the first tile (and its mask)
   tile_barrier();
+  if (rot && my_row < a.Lq && my_p >= 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+      u32x4 lo = qf[ks], hi = qf[ks + KS / 2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x4& c = rc[ks][e >> 1];
+        const f32x4& sn = rs[ks][e >> 1];
+        float u0, w0, u1, w1;
+        rot_pair(half_to_f32<IS_BF16>((uint16_t)(lo[e] & 0xffffu)), half_to_f32<IS_BF16>((uint16_t)(hi[e] & 0xffffu)),
+                 c[2 * (e & 1)], sn[2 * (e & 1)], u0, w0);
+        rot_pair(half_to_f32<IS_BF16>((uint16_t)(lo[e] >> 16)), half_to_f32<IS_BF16>((uint16_t)(hi[e] >> 16)),
+                 c[2 * (e & 1) + 1], sn[2 * (e & 1) + 1], u1, w1);
+        lo[e] = pack2<IS_BF16>(u0, u1);
+        hi[e] = pack2<IS_BF16>(w0, w1);
+      }
+      qf[ks] = lo;
+      qf[ks + KS / 2] = hi;
+    }
+  }
 
   f32x16 sc[2];
   u32x4 pb[2][2];

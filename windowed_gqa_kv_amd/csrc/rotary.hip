@@ -120,10 +120,7 @@ __global__ __launch_bounds__(256) void rotary_kernel(RotaryArgs a) {
     Elem<kF32>::load<P>(a.sin + pos * half + i0, sn);
     float u[P], w[P];
 #pragma unroll
-    for (int e = 0; e < P; ++e) {
-      u[e] = x[e] * cs[e] - y[e] * sn[e];
-      w[e] = y[e] * cs[e] + x[e] * sn[e];
-    }
+    for (int e = 0; e < P; ++e) rot_pair(x[e], y[e], cs[e], sn[e], u[e], w[e]);
     E::template store<P>(dst + E::kBytes * i0, u);
     E::template store<P>(dst + E::kBytes * (i0 + half), w);
   } else {
