@@ -29,11 +29,14 @@ def _add_mask(seed, shape, neg_inf=0.05):
     return torch.from_numpy(m)
 
 
-def _block_sparse(seed, Lq, Lk, block=64):
-    """Whole 64-key blocks cleared per 16-row group, about half of them."""
+def _block_sparse(seed, Lq, Lk, block=64, rows=16):
+    """Whole 64-key blocks cleared per group of `rows` rows, about half of
+    them (with 128-row groups a cleared block is a tile no wave of a
+    workgroup needs, which the matrix-core prefill neither loads nor
+    computes)."""
     rng = np.random.default_rng(seed)
-    keep = rng.random(((Lq + 15) // 16, (Lk + block - 1) // block)) < 0.5
-    m = np.repeat(np.repeat(keep, 16, 0), block, 1)[:Lq, :Lk]
+    keep = rng.random(((Lq + rows - 1) // rows, (Lk + block - 1) // block)) < 0.5
+    m = np.repeat(np.repeat(keep, rows, 0), block, 1)[:Lq, :Lk]
     return torch.from_numpy(m[None, None])
 
 
@@ -59,6 +62,9 @@ PREFILL = [
     ("f16", 2, 8, 4, 256, 130, 256, -1, 30.0, False, (256, 100), "add", "bh"),  # matrix core, 256, softcap
     ("bf16", 2, 8, 2, 32, 300, 320, 128, 0.0, True, None, "sparse", "11"),    # matrix core, head size 32
     ("f16", 1, 4, 2, 32, 96, 200, -1, 20.0, False, None, "add", "1h"),        # matrix core, 32, softcap
+    ("bf16", 1, 8, 2, 128, 640, 1280, 500, 0.0, True, None, "sparse128", "11"),  # whole tiles skipped
+    ("f16", 2, 16, 4, 64, 384, 896, -1, 20.0, False, (896, 500), "sparse128", "11"),
+    ("bf16", 1, 16, 8, 256, 256, 768, -1, 0.0, False, None, "sparse128", "11"),
     ("f32", 1, 4, 2, 32, 64, 64, 16, 0.0, True, None, "bool", "11"),
     ("bf16", 1, 8, 2, 128, 300, 300, -1, 0.0, False, None, "sparse", "11"),
     ("f32", 2, 4, 2, 64, 70, 90, 20, 5.0, False, (90, 33), "add", "b1"),
@@ -79,8 +85,8 @@ def test_masked_prefill_matches_oracle(gpu, case):
     if kind == "bool":
         mask = _bool_mask(Lq * 7 + Lk, shape)
         mask[..., 3, :] = False  # a row with no key left
-    elif kind == "sparse":
-        mask = _block_sparse(Lq, Lq, Lk)
+    elif kind in ("sparse", "sparse128"):
+        mask = _block_sparse(Lq, Lq, Lk, rows=16 if kind == "sparse" else 128)
         mask[..., 7, :] = False  # a row with no key left
     else:
         mask = _add_mask(Lq * 11 + Lk, shape)
@@ -95,8 +101,8 @@ def test_masked_prefill_matches_oracle(gpu, case):
                           nonpad_kv_seqlen=None if d["nonpad"] is None else d["nonpad"].numpy(),
                           mask=mask.numpy() if kind != "add" else mask.numpy().astype(np.float64))
     compare(out, want, dtype, f"masked prefill {case}")
-    if kind in ("bool", "add", "sparse"):
-        row = {"bool": 3, "add": 5, "sparse": 7}[kind]
+    if kind in ("bool", "add", "sparse", "sparse128"):
+        row = {"bool": 3, "add": 5, "sparse": 7, "sparse128": 7}[kind]
         assert not out[:, :, row].any(), "a row with every key masked must be zero"
 
 

@@ -327,7 +327,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
       }
     }
   };
-  uint64_t mk_cur[4] = {0, 0, 0, 0}, mk_nxt[4] = {0, 0, 0, 0};
+  // mk_cur: this tile's runs; mk_nxt: the next tile's; mk_nn: the one after,
+  // loaded two tiles ahead so that the workgroup can vote on a tile before
+  // its DMA would be issued.
+  uint64_t mk_cur[4] = {0, 0, 0, 0}, mk_nxt[4] = {0, 0, 0, 0}, mk_nn[4] = {0, 0, 0, 0};
+  // Whether any wave needs a tile (its band reaches the tile and the mask
+  // leaves one of its rows a key there): one flag per wave and tile parity.
+  // A tile no wave needs is neither loaded nor computed.
+  __shared__ int wg_need[2][kWaves];
+  bool mk_full = false;  // the current tile's mask keeps every key of this wave's rows
   // Additive mask: the same runs as fp32 (two aligned 16-byte loads each),
   // loaded at the start of the tile that uses them: the K Q^T MFMAs cover the
   // latency, and every tile is evaluated in full.  bias / scale in raw score
@@ -443,11 +451,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
           acc[r2] = (j < my_lo || j > my_hi) ? -INFINITY : acc[r2];
         }
       }
-      if constexpr (MASK == 1) {  // the caller mask, on every tile
+      if constexpr (MASK == 1) {  // the caller mask, unless it keeps every key of the wave's tile
+        if (!mk_full) {
 #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) {
-          const uint64_t run = mk_cur[2 * sub + (r2 >> 3)];
-          acc[r2] = ((run >> (8 * (r2 & 7))) & 0xffu) ? acc[r2] : -INFINITY;
+          for (int r2 = 0; r2 < 16; ++r2) {
+            const uint64_t run = mk_cur[2 * sub + (r2 >> 3)];
+            acc[r2] = ((run >> (8 * (r2 & 7))) & 0xffu) ? acc[r2] : -INFINITY;
+          }
         }
       }
       if constexpr (MASK == 2) {  // -inf (or NaN) removes the key
@@ -540,10 +550,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
 
   // ---- schedule: per tile, K Q^T (the next tile's loads riding along), the
   // softmax, P V; then wait for the next tile and meet ----
+  // a wave's need of the tile at kb (wave-uniform)
+  auto wave_needs = [&](int kb, const uint64_t (&mk)[4]) -> int {
+    bool b0, b1;
+    active(kb, b0, b1);
+    const bool n0 = __any((mk[0] | mk[1]) != 0), n1 = __any((mk[2] | mk[3]) != 0);
+    return (b0 && n0) || (b1 && n1);
+  };
   if (nblk > 0) dma_tile(kv_lo, 0);
-  if constexpr (MASK == 1)
+  if constexpr (MASK == 1) {
     if (nblk > 0) mask_load(kv_lo, mk_nxt);
+    if (nblk > 1) mask_load(kv_lo + BN, mk_nn);
+  }
   __builtin_amdgcn_s_waitcnt(0);  // Q registers, the first tile (and its mask)
+  if constexpr (MASK == 1) {
+    if (nblk > 1) {
+      const int nd = wave_needs(kv_lo + BN, mk_nn);
+      if (lane == 0) wg_need[1][w] = nd;
+    }
+  }
   tile_barrier();
   if (rot && my_row < a.Lq && my_p >= 0) {
 #pragma unroll
@@ -577,20 +602,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
     // at once by a wave with nothing to compute here): a wave that issued all
     // of them back to back would stall behind the other waves' loads.
     const bool next = it + 1 < nblk;
-    auto dma_at = [&](int i) {
-      if (next) dma_part(kb + BN, ST ^ 1, i);
-    };
+    bool load_next = next;
     bool a0, a1;
     active(kb, a0, a1);
     if constexpr (MASK == 1) {
-      // this tile's mask landed with the last tile's loads; fetch the next
-      // one, and skip sub-tiles whose keys the mask clears for all 32 rows
+      // the workgroup's vote on the next tile (flags written before the last
+      // barrier); this tile's runs landed with an earlier tile's loads; fetch
+      // the runs two tiles ahead, and skip sub-tiles whose keys the mask
+      // clears for all 32 rows
+      if (next)
+        load_next = (wg_need[(it + 1) & 1][0] | wg_need[(it + 1) & 1][1] | wg_need[(it + 1) & 1][2] |
+                     wg_need[(it + 1) & 1][3]) != 0;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) mk_cur[x] = mk_nxt[x];
-      if (next) mask_load(kb + BN, mk_nxt);
+      for (int x = 0; x < 4; ++x) {
+        mk_cur[x] = mk_nxt[x];
+        mk_nxt[x] = mk_nn[x];
+      }
+      if (it + 2 < nblk) mask_load(kb + 2 * BN, mk_nn);
       a0 = a0 && __any((mk_cur[0] | mk_cur[1]) != 0);
       a1 = a1 && __any((mk_cur[2] | mk_cur[3]) != 0);
+      // every byte of every run nonzero (no zero byte: the has-zero-byte bit
+      // trick on each run) in every lane: the tile keeps all its keys
+      constexpr uint64_t kOnes = 0x0101010101010101ull, kHigh = 0x8080808080808080ull;
+      uint64_t zero = 0;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) zero |= (mk_cur[x] - kOnes) & ~mk_cur[x] & kHigh;
+      mk_full = __all(zero == 0);
     }
+    auto dma_at = [&](int i) {
+      if (load_next) dma_part(kb + BN, ST ^ 1, i);
+    };
     if constexpr (MASK == 2)
       if (a0 || a1) bias_load(kb);
     if (a0 || a1) {
@@ -600,12 +641,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
 #pragma unroll
       for (int q = 0; q < 4; ++q) softmax_exp(sc[q >> 1], q & 1, pb[q >> 1][q & 1]);
       pv(stage_tag, pb, [] {}, [](int) {});
-    } else if (next) {
+    } else if (load_next) {
       dma_tile(kb + BN, ST ^ 1);
     }
     // this wave's loads of the next tile have landed; after the barrier every
     // wave's have, and nobody reads this tile's stage any more
     wait_vm<0>();
+    if constexpr (MASK == 1) {
+      // this wave's need of the tile after next, for the vote at its start
+      if (it + 2 < nblk) {
+        const int nd = wave_needs(kb + 2 * BN, mk_nn);
+        if (lane == 0) wg_need[it & 1][w] = nd;
+      }
+    }
     tile_barrier();
   };
   for (int it = 0; it < nblk; it += 2) {
