@@ -273,8 +273,9 @@ gqa_status gqa_prefill_rotary(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t Lk
  * position total_b - curr + t, total_b = seqlens_k[b] + 1, which is also its
  * cache slot (a single generated token: position seqlens_k[b]); with
  * attrs.rolling_cache the slot is that position mod capacity, positions may
- * pass the capacity, and rows whose position is at or past tables->max_pos
- * are left unwritten (the host cannot see the lengths).
+ * pass the capacity, and K and q_rot rows whose position is at or past
+ * tables->max_pos are left unwritten (the host cannot see the lengths; the
+ * V rows are still copied).
  *   q, q_rot [B, Hq, curr, D] (q_rot may be q itself); k_new, v_new, k_cache,
  *   v_cache and seqlens_k as in gqa_append_kv; tables as above.
  * A batch with total_b < curr, or (without rolling_cache) total_b > capacity,
@@ -385,6 +386,31 @@ gqa_status gqa_decode_fp8_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64
                                  const int32_t* seqlens_k, const float* head_sink,
                                  float k_scale, float v_scale, const gqa_mask* mask,
                                  void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* The kernel that computed the attention of this thread's last call, so a
+ * caller can tell a fast path from the slow one (the pages' streaming path
+ * serves every accepted type, "Attention Kernel Design", section "Compute
+ * paths"; here it is the fallback):
+ *   GQA_PATH_NONE            no attention ran: a failed or empty call, or a
+ *                            call without attention (append, rotary);
+ *   GQA_PATH_MATRIX_PREFILL  the matrix-core prefill (bf16/fp16, head size
+ *                            32/64/128/256);
+ *   GQA_PATH_MATRIX_DECODE   the matrix-core split-KV decode (bf16/fp16, head
+ *                            size 64/128/256, at most 2048 row tiles of 16
+ *                            query rows per call);
+ *   GQA_PATH_STREAMING       the one-wavefront-per-row fp32 kernel: fp32
+ *                            plans, other head sizes, K/V row strides of 2^24
+ *                            elements or more, masks whose layout the matrix
+ *                            cores cannot read, decode calls with more row
+ *                            tiles -- correct, and tens of times slower.
+ * Set when the call enqueues its launch; thread-local. */
+typedef enum {
+  GQA_PATH_NONE = 0,
+  GQA_PATH_MATRIX_PREFILL = 1,
+  GQA_PATH_MATRIX_DECODE = 2,
+  GQA_PATH_STREAMING = 3
+} gqa_path;
+gqa_path gqa_last_path(void);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * Every rejection names the argument and the rule it breaks: the "rejected

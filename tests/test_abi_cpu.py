@@ -314,6 +314,14 @@ def test_fp8_validation():
     assert dm(ok, Bn=0) == B.GQA_OK
 
 
+def test_last_path_is_none_after_failed_or_empty_calls():
+    h = plan()
+    assert _prefill(h, Lq=17) == B.GQA_ERR_CAPACITY
+    assert B.gqa_last_path() == B.GQA_PATH_NONE
+    assert _prefill(h, Bn=0) == B.GQA_OK
+    assert B.gqa_last_path() == B.GQA_PATH_NONE
+
+
 def test_last_error_is_thread_local_and_specific():
     import threading
     B.gqa_plan(attrs(num_heads=0), 1, 1, 1)

@@ -229,3 +229,32 @@ def test_prefill_rotary_full_size_long_prompt(gpu):
     b = plan.prefill_rotary(q, k_r, d["v"].cuda(), cos, sin)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_append_kv_rotary_rolling_past_the_tables(gpu):
+    """A rolling cache's positions pass the capacity and the host cannot see
+    them: rows whose position is at or past the tables are not turned -- their
+    K slot and q_rot row are left as they were -- while V is still copied;
+    rows inside the tables are turned as usual."""
+    W, curr, D = 8, 2, 64
+    C = W + curr - 1
+    max_pos = 40
+    w = Workload("rotpast", "decode", "bf16", B=2, Hq=4, Hkv=2, D=D, Lq=curr, Lk=C, window=W,
+                 seqlens=("list", [max_pos, 20]), seed=83)  # batch 0: positions 39, 40; batch 1: 19, 20
+    d = generate(w)
+    cos, sin = rotary_tables(max_pos, D)
+    plan = make_plan(w, rolling_cache=True)
+    kc, vc = d["k_cache"].cuda(), d["v_cache"].cuda()
+    q = d["q"].cuda()
+    q_rot = torch.zeros_like(q)
+    plan.append_kv_rotary(q, d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, d["seqlens_k"].cuda(),
+                          cos.cuda(), sin.cuda(), q_rot=q_rot)
+    torch.cuda.synchronize()
+    # batch 0, token 0 at position 39 (inside the tables), token 1 at 40 (past them)
+    s39, s40 = 39 % C, 40 % C
+    _check_turned(kc[0, :, s39].cpu()[None, :, None], d["k_new"][0, :, 0][None, :, None], np.array([39]), cos, sin,
+                  "bf16", "K inside the tables")
+    assert torch.equal(kc[0, :, s40].cpu(), d["k_cache"][0, :, s40]), "K past the tables was written"
+    assert torch.equal(vc[0, :, s39].cpu(), d["v_new"][0, :, 0]) and torch.equal(vc[0, :, s40].cpu(), d["v_new"][0, :, 1])
+    assert not q_rot[0, :, 1].any(), "q_rot past the tables was written"
+    _check_turned(q_rot[1].cpu(), d["q"][1], np.array([19, 20])[None, :], cos, sin, "bf16", "batch 1 q")

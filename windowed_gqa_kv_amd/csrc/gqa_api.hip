@@ -35,6 +35,9 @@ namespace {
 constexpr int64_t kMaxLen = int64_t(1) << 30;  // keeps every position in int32 arithmetic
 
 thread_local std::string g_err;
+// The kernel that computed the attention of this thread's last call (a
+// gqa_path value): set when a launch is enqueued, reset at every entry.
+thread_local int g_path = GQA_PATH_NONE;
 
 gqa_status fail(gqa_status st, const char* fmt, ...) {
   char buf[512];
@@ -61,8 +64,23 @@ gqa_status check_tensor(const char* name, const gqa_tensor& t, int esz) {
   return GQA_OK;
 }
 
+hipError_t path_prefill_mfma(const gqa::AttnArgs& a, int dtype, bool softcap, hipStream_t stream) {
+  g_path = GQA_PATH_MATRIX_PREFILL;
+  return gqa::launch_prefill_mfma(a, dtype, softcap, stream);
+}
+hipError_t path_decode_mfma(const gqa::AttnArgs& a, int dtype, bool softcap, const gqa::DecodeGeometry& geo,
+                            float* ws, hipStream_t stream) {
+  g_path = GQA_PATH_MATRIX_DECODE;
+  return gqa::launch_decode_mfma(a, dtype, softcap, geo, ws, stream);
+}
+hipError_t path_streaming(const gqa::AttnArgs& a, int dtype, hipStream_t stream) {
+  g_path = GQA_PATH_STREAMING;
+  return gqa::launch_attn_generic(a, dtype, stream);
+}
+
 gqa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return GQA_OK;
+  g_path = GQA_PATH_NONE;
   return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -120,6 +138,7 @@ gqa_status check_sink(const gqa_plan_s* p, const float* head_sink) {
 
 GQA_API gqa_status gqa_plan(const gqa_attrs* attrs, int32_t max_batch, int32_t max_q_len,
                             int64_t max_kv_len, gqa_plan_t* out_plan) {
+  g_path = GQA_PATH_NONE;
   if (out_plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "out_plan is NULL");
   *out_plan = nullptr;
   if (attrs == nullptr) return fail(GQA_ERR_INVALID_ARG, "attrs is NULL");
@@ -183,6 +202,7 @@ GQA_API gqa_status gqa_prefill(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t L
                                gqa_tensor k, gqa_tensor v, gqa_tensor out,
                                const int64_t* nonpad_kv_seqlen, const float* head_sink,
                                void* workspace, size_t ws_bytes, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   (void)workspace;
   (void)ws_bytes;
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
@@ -212,15 +232,16 @@ GQA_API gqa_status gqa_prefill(gqa_plan_t plan, int32_t B, int32_t Lq, int64_t L
   // the matrix-core kernel addresses a 64-row K/V tile with 32-bit offsets
   const bool small_strides = a.k_ss < (int64_t(1) << 24) && a.v_ss < (int64_t(1) << 24);
   if (Lk > 0 && small_strides && gqa::prefill_mfma_supported(dtype, plan->attrs.head_size))
-    e = gqa::launch_prefill_mfma(a, dtype, plan->attrs.softcap > 0, stream);
+    e = path_prefill_mfma(a, dtype, plan->attrs.softcap > 0, stream);
   else
-    e = gqa::launch_attn_generic(a, dtype, stream);
+    e = path_streaming(a, dtype, stream);
   return hip_status(e, "prefill launch");
 }
 
 GQA_API gqa_status gqa_append_kv(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
                                  gqa_tensor k_new, gqa_tensor v_new, gqa_tensor k_cache,
                                  gqa_tensor v_cache, const int32_t* seqlens_k, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -275,6 +296,7 @@ GQA_API gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t 
                               gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
                               const int32_t* seqlens_k, const float* head_sink, void* workspace,
                               size_t ws_bytes, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   return decode_impl(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, workspace,
                      ws_bytes, hip_stream, false);
 }
@@ -282,6 +304,7 @@ GQA_API gqa_status gqa_decode(gqa_plan_t plan, int32_t B, int32_t curr, int64_t 
 GQA_API gqa_status gqa_decode_noalloc(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
                                       gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
                                       const int32_t* seqlens_k, const float* head_sink, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   return decode_impl(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, nullptr, 0,
                      hip_stream, true);
 }
@@ -290,6 +313,7 @@ GQA_API gqa_status gqa_append_decode(gqa_plan_t plan, int32_t B, int32_t curr, i
                                      gqa_tensor k_new, gqa_tensor v_new, gqa_tensor k_cache, gqa_tensor v_cache,
                                      gqa_tensor out, const int32_t* seqlens_k, const float* head_sink,
                                      void* workspace, size_t ws_bytes, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   return decode_impl(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, workspace,
                      ws_bytes, hip_stream, false, &k_new, &v_new);
 }
@@ -436,10 +460,10 @@ gqa_status decode_impl(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacit
         return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     }
     if (geo.fits)
-      return hip_status(gqa::launch_decode_mfma(a, dtype, softcap, geo, ws, stream), "decode launch");
+      return hip_status(path_decode_mfma(a, dtype, softcap, geo, ws, stream), "decode launch");
   }
   if ((st = append_first()) != GQA_OK) return st;
-  return hip_status(gqa::launch_attn_generic(a, dtype, stream), "decode launch");
+  return hip_status(path_streaming(a, dtype, stream), "decode launch");
 }
 
 }  // namespace
@@ -474,6 +498,7 @@ void set_job(gqa::RotaryArgs& a, int j, const gqa_tensor& src, const gqa_tensor&
 GQA_API gqa_status gqa_apply_rotary(gqa_plan_t plan, int32_t B, int32_t H, int32_t L, int64_t pos0,
                                     gqa_tensor x, gqa_tensor y, const gqa_rotary_tables* tables,
                                     void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || H < 0 || L < 0 || pos0 < 0) return fail(GQA_ERR_INVALID_ARG, "B, H, L and pos0 must be >= 0");
   if (B > 65535 || H > 65535) return fail(GQA_ERR_UNSUPPORTED, "B and H must be <= 65535");
@@ -503,6 +528,7 @@ GQA_API gqa_status gqa_prefill_rotary(gqa_plan_t plan, int32_t B, int32_t Lq, in
                                       gqa_tensor k, gqa_tensor v, gqa_tensor out,
                                       const int64_t* nonpad_kv_seqlen, const float* head_sink,
                                       const gqa_rotary_tables* tables, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || Lq < 0 || Lk < 0) return fail(GQA_ERR_INVALID_ARG, "B, Lq and Lk must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -535,14 +561,15 @@ GQA_API gqa_status gqa_prefill_rotary(gqa_plan_t plan, int32_t B, int32_t Lq, in
   a.rot_cos = tables->cos;
   a.rot_sin = tables->sin;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  if (Lk == 0) return hip_status(gqa::launch_attn_generic(a, dtype, stream), "prefill launch");  // zeros
-  return hip_status(gqa::launch_prefill_mfma(a, dtype, plan->attrs.softcap > 0, stream), "prefill_rotary launch");
+  if (Lk == 0) return hip_status(path_streaming(a, dtype, stream), "prefill launch");  // zeros
+  return hip_status(path_prefill_mfma(a, dtype, plan->attrs.softcap > 0, stream), "prefill_rotary launch");
 }
 
 GQA_API gqa_status gqa_append_kv_rotary(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
                                         gqa_tensor q, gqa_tensor q_rot, gqa_tensor k_new, gqa_tensor v_new,
                                         gqa_tensor k_cache, gqa_tensor v_cache, const int32_t* seqlens_k,
                                         const gqa_rotary_tables* tables, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -610,6 +637,7 @@ GQA_API gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, in
                                       gqa_tensor k, gqa_tensor v, gqa_tensor out,
                                       const int64_t* nonpad_kv_seqlen, const float* head_sink,
                                       const gqa_mask* mask, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || Lq < 0 || Lk < 0) return fail(GQA_ERR_INVALID_ARG, "B, Lq and Lk must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -646,15 +674,16 @@ GQA_API gqa_status gqa_prefill_masked(gqa_plan_t plan, int32_t B, int32_t Lq, in
   a.bias_mul = 1.0f / plan->scale;
   if (Lk > 0 && small_strides && gqa::prefill_mfma_supported(dtype, plan->attrs.head_size) &&
       aligned)
-    return hip_status(gqa::launch_prefill_mfma(a, dtype, plan->attrs.softcap > 0.0f, stream),
+    return hip_status(path_prefill_mfma(a, dtype, plan->attrs.softcap > 0.0f, stream),
                       "masked prefill launch");
-  return hip_status(gqa::launch_attn_generic(a, dtype, stream), "masked prefill launch");
+  return hip_status(path_streaming(a, dtype, stream), "masked prefill launch");
 }
 
 GQA_API gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
                                      gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
                                      const int32_t* seqlens_k, const float* head_sink, const gqa_mask* mask,
                                      void* workspace, size_t ws_bytes, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -694,11 +723,11 @@ GQA_API gqa_status gqa_decode_masked(gqa_plan_t plan, int32_t B, int32_t curr, i
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
       return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     if (geo.fits)
-      return hip_status(gqa::launch_decode_mfma(a, dtype, plan->attrs.softcap > 0.0f, geo,
+      return hip_status(path_decode_mfma(a, dtype, plan->attrs.softcap > 0.0f, geo,
                                                 reinterpret_cast<float*>(workspace), stream),
                         "masked decode launch");
   }
-  return hip_status(gqa::launch_attn_generic(a, dtype, stream), "masked decode launch");
+  return hip_status(path_streaming(a, dtype, stream), "masked decode launch");
 }
 
 namespace {
@@ -723,6 +752,7 @@ GQA_API gqa_status gqa_append_kv_fp8(gqa_plan_t plan, int32_t B, int32_t curr, i
                                      gqa_tensor k_new, gqa_tensor v_new, gqa_tensor k_cache,
                                      gqa_tensor v_cache, const int32_t* seqlens_k, float k_scale,
                                      float v_scale, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -822,7 +852,7 @@ gqa_status decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity
     return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   if (!geo.fits)
     return fail(GQA_ERR_UNSUPPORTED, "FP8 caches: at most %d row tiles per call", 2048);
-  return hip_status(gqa::launch_decode_mfma(a, (int)plan->attrs.dtype, plan->attrs.softcap > 0, geo,
+  return hip_status(path_decode_mfma(a, (int)plan->attrs.dtype, plan->attrs.softcap > 0, geo,
                                             reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(hip_stream)),
                     "decode_fp8 launch");
 }
@@ -833,6 +863,7 @@ GQA_API gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int6
                                   gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
                                   const int32_t* seqlens_k, const float* head_sink, float k_scale,
                                   float v_scale, void* workspace, size_t ws_bytes, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   return decode_fp8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scale, v_scale,
                     nullptr, workspace, ws_bytes, hip_stream);
 }
@@ -842,9 +873,12 @@ GQA_API gqa_status gqa_decode_fp8_masked(gqa_plan_t plan, int32_t B, int32_t cur
                                          const int32_t* seqlens_k, const float* head_sink, float k_scale,
                                          float v_scale, const gqa_mask* mask, void* workspace, size_t ws_bytes,
                                          void* hip_stream) {
+  g_path = GQA_PATH_NONE;
   if (mask == nullptr) return fail(GQA_ERR_INVALID_ARG, "mask is NULL");
   return decode_fp8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scale, v_scale,
                     mask, workspace, ws_bytes, hip_stream);
 }
 
 GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }
+
+GQA_API gqa_path gqa_last_path(void) { return (gqa_path)g_path; }

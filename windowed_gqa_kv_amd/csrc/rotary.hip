@@ -103,7 +103,11 @@ __global__ __launch_bounds__(256) void rotary_kernel(RotaryArgs a) {
   } else {
     pos = a.pos0 + l;
   }
-  if (pos < 0 || pos >= a.max_pos) return;  // unreachable after the host checks
+  // A position the tables do not cover happens only in a decode step on a
+  // rolling cache (positions pass the capacity, and the host cannot see the
+  // lengths): a row to be turned is then left unwritten; a copied row (V)
+  // needs no table and is written.
+  if (a.turn[j] && (pos < 0 || pos >= a.max_pos)) return;
   const int half = a.D / 2;
   const int i0 = P * c;
   const char* src = reinterpret_cast<const char*>(a.src[j]) +
