@@ -26,9 +26,12 @@ peak) and the speculative-decode workload the same way; `rotary` times the
 rotary embedding of the long prompt's Q and K (GB/s against HBM) and a decode
 step's append with rotary beside the plain append; `rolling` times the
 speculative-decode workload against a rolling cache of W + curr - 1 slots;
-`masks` times the long prompt through the masked (streaming) kernel with an
-all-True and a block-sparse boolean mask; `fp8` times the headline decode on
-FP8 (E4M3) caches.
+`masks` times the long prompt through the masked matrix-core prefill with an
+all-True and block-sparse boolean masks (16x64 and 128x64 blocks), an
+additive one and one with softcap, beside the unmasked prefill; `fp8` times
+the headline decode on FP8 (E4M3) caches; `peaks_measured` reports the dense
+bf16 MFMA rate and shader clock measured on the device and a 1 GiB copy's
+rate, for context (fractions stay against the published peaks).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
        [--no-cpu-baseline] [--workload NAME]
@@ -215,12 +218,12 @@ def bench_decode(w, steps, warmup, replicas):
                 decode_only_ms=dec_ms, decode_bytes=dec_bytes, replicas=R, inputs=d)
 
 
-def bench_prefill(w, steps, warmup):
+def bench_prefill(w, steps, warmup, d=None):
     import torch
     from windowed_gqa_kv_amd import binding, work
     from windowed_gqa_kv_amd.inputs import generate
 
-    d = generate(w)
+    d = d if d is not None else generate(w)
     plan = binding.Plan(w.Hq, w.Hkv, w.D, dtype=w.dtype, scale=w.sm_scale, local_window_size=w.window,
                         softcap=w.softcap, smooth_softmax=w.smooth_softmax, use_head_sink=w.head_sink,
                         is_causal=w.causal, max_batch=w.B, max_q_len=w.Lq, max_kv_len=w.Lk)
@@ -287,7 +290,31 @@ def bench_rotary(steps, warmup):
                      "bytes": bq + bk, "achieved": round((bq + bk) / ((ms_q + ms_k) / 1e3) / 1e9, 2),
                      "unit": "GB/s"}
     res["prompt"]["frac"] = round(res["prompt"]["achieved"] / PEAK_HBM_GBS, 4)
-    del qs, ks, qo, ko
+    # the prompt's attention with Q turned inside the prefill
+    # (gqa_prefill_rotary, K turned once beforehand) against the turn as its
+    # own pass followed by gqa_prefill; Q rotates over the same 8 replicas
+    v0 = torch.empty_like(ks[0]).normal_().mul_(0.5)
+    out = torch.empty_like(qo)
+    ev2 = {"prefill_rotary": _events(steps), "apply_rotary_q_then_prefill": _events(steps)}
+    for i in range(2):
+        plan.prefill_rotary(qs[i], ko, v0, cos, sin, out)
+        plan.apply_rotary(qs[i], 0, cos, sin, qo)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        a, b = ev2["prefill_rotary"][i]
+        a.record()
+        plan.prefill_rotary(qs[i % R], ko, v0, cos, sin, out)
+        b.record()
+        a, b = ev2["apply_rotary_q_then_prefill"][i]
+        a.record()
+        plan.apply_rotary(qs[(i + R // 2) % R], 0, cos, sin, qo)
+        plan.prefill(qo, ko, v0, out)
+        b.record()
+    torch.cuda.synchronize()
+    res["prompt_attention"] = {name: round(sorted(x.elapsed_time(y) for x, y in ev)[len(ev) // 2], 5)
+                               for name, ev in ev2.items()}
+    res["prompt_attention"]["unit"] = "ms (median of events around each, Q cold)"
+    del qs, ks, qo, ko, v0, out
     torch.cuda.empty_cache()
 
     wd = WORKLOADS[2]
@@ -409,9 +436,23 @@ def bench_masks(steps):
     rng = np.random.default_rng(5)
     keep = rng.random(((w.Lq + 15) // 16, (w.Lk + 63) // 64)) < 0.5
     sparse = np.repeat(np.repeat(keep, 16, 0), 64, 1)[:w.Lq, :w.Lk]
+    keep128 = rng.random(((w.Lq + 127) // 128, (w.Lk + 63) // 64)) < 0.5
+    sparse128 = np.repeat(np.repeat(keep128, 128, 0), 64, 1)[:w.Lq, :w.Lk]
     res = {"workload": w.name}
     add = np.where(sparse, 0.0, -np.inf).astype(np.float32)
+    out0 = torch.empty_like(q)
+    plan.prefill(q, k, v, out0)
+    ev0 = _events(steps)
+    torch.cuda.synchronize()
+    for a, b in ev0:
+        a.record()
+        plan.prefill(q, k, v, out0)
+        b.record()
+    torch.cuda.synchronize()
+    res["unmasked_kernel_ms"] = round(sum(a.elapsed_time(b) for a, b in ev0) / steps, 4)
+    del out0
     for name, m, p in (("all_true", np.ones((w.Lq, w.Lk), bool), plan), ("block_sparse", sparse, plan),
+                       ("block_sparse_128x64", sparse128, plan),
                        ("block_sparse_additive", add, plan), ("block_sparse_softcap50", sparse, capped)):
         md = torch.from_numpy(m)[None, None].cuda()
         m = m if m.dtype == bool else m > -np.inf
@@ -514,6 +555,80 @@ def bench_fp8(reps):
             "bytes_per_launch": b, "achieved": round(b / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
             "frac": round(b / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "bool_mask_kernel_ms": round(ms_masked, 5)}
+
+
+def peaks_measured():
+    """Context for the fractions (which stay against the published peaks):
+    the dense bf16 matrix rate and the shader clock measured on this device
+    by the library's probe (back-to-back register-operand MFMAs, shader-clock
+    and 100 MHz stamps per wave), and a plain 1 GiB device copy's rate."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    from windowed_gqa_kv_amd import binding
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 4000
+    stamps = torch.zeros(blocks * 4 * 4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(blocks * 4, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sp, kp = ctypes.c_void_p(stamps.data_ptr()), ctypes.c_void_p(sink.data_ptr())
+    binding.check(0 if binding.gqa_probe_mfma_peak(blocks, 200, sp, kp, stream) == 0 else 4)
+    best = None
+    for _ in range(3):
+        e0, e1 = _events(1)[0]
+        e0.record()
+        rc = binding.gqa_probe_mfma_peak(blocks, iters, sp, kp, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError("MFMA probe launch failed")
+        ms = e0.elapsed_time(e1)
+        st = stamps.view(-1, 4).cpu().numpy().astype(np.float64)
+        clk = float(np.median((st[:, 1] - st[:, 0]) / ((st[:, 3] - st[:, 2]) / 1e8)))
+        if best is None or ms < best[0]:
+            best = (ms, clk)
+    ms, clk = best
+    flops = blocks * 4 * iters * 8 * 32768
+    x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    ev = _events(5)
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        y.copy_(x)
+        b.record()
+    torch.cuda.synchronize()
+    cms = min(a.elapsed_time(b) for a, b in ev)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(flops / (ms / 1e3) / 1e12, 1),
+            "shader_clock_ghz": round(clk / 1e9, 3),
+            "dense_bf16_peak_at_that_clock_tflops": round(cus * 4 * 1024 * clk / 1e12, 1),
+            "published_peaks": {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS},
+            "copy_1gib_gbs": round(2 * (1 << 30) / (cms / 1e3) / 1e9, 1),
+            "note": "fractions are against the published peaks; these are measured on this device for context"}
+
+
+def bench_prefill_d256(steps):
+    """A prompt at head size 256 (the speculative-decode workload's model:
+    Hq 16, Hkv 8, sink, softcap 50) of 8192 tokens with a 4096-key window, on
+    the matrix-core prefill."""
+    import torch
+    from windowed_gqa_kv_amd import binding, work
+    from windowed_gqa_kv_amd.inputs import Workload, generate
+
+    w = Workload("prefill_d256_bf16", "prefill", "bf16", B=1, Hq=16, Hkv=8, D=256, Lq=8192, Lk=8192,
+                 window=4096, head_sink=True, softcap=50.0, value_scale=0.5, seed=1006)
+    d = generate(w)
+    r = bench_prefill(w, steps, 3, d)
+    tf = r["flops"] / (r["kernel_ms"] / 1e3) / 1e12
+    return {"workload": w.name, "config": {"B": 1, "Hq": 16, "Hkv": 8, "D": 256, "L": 8192, "window": 4096,
+                                           "head_sink": True, "softcap": 50.0},
+            "kernel_ms": round(r["kernel_ms"], 5), "achieved": round(tf, 2), "unit": "TFLOP/s",
+            "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def cpu_baseline(w, d, budget_s=12.0):
@@ -642,12 +757,15 @@ def main():
                                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                                        "kernel_ms": round(rp["kernel_ms"], 5), "flops_per_launch": rp["flops"]}})
             torch.cuda.empty_cache()
+        extra.append(bench_prefill_d256(args.extra_steps))
+        torch.cuda.empty_cache()
         line["extra"] = extra
         line["rotary"] = bench_rotary(args.extra_steps, 3)
         line["rolling"] = bench_rolling(5)
         line["masks"] = bench_masks(3)
         line["fp8"] = bench_fp8(5)
 
+    line["peaks_measured"] = peaks_measured()
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, r["inputs"])
     print(json.dumps(line), flush=True)
 

@@ -21,7 +21,10 @@ FAKE = 1 << 20  # a 16-byte aligned non-NULL address; never dereferenced
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    """Functions declared by every header under include/ (the attention ABI
+    and the measurement probe)."""
+    src = "".join(open(os.path.join(ROOT, "include", f)).read()
+                  for f in sorted(os.listdir(os.path.join(ROOT, "include"))) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", src)))
 

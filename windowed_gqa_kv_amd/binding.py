@@ -34,7 +34,7 @@ EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
             "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
             "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_append_decode", "gqa_prefill_rotary",
-            "gqa_last_path", "gqa_last_error")
+            "gqa_last_path", "gqa_last_error", "gqa_probe_mfma_peak")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
@@ -130,6 +130,8 @@ def load():
     lib.gqa_append_decode.restype = ctypes.c_int
     lib.gqa_prefill_rotary.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, RT, P]
     lib.gqa_prefill_rotary.restype = ctypes.c_int
+    lib.gqa_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P]
+    lib.gqa_probe_mfma_peak.restype = ctypes.c_int
     lib.gqa_last_path.argtypes = []
     lib.gqa_last_path.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
@@ -240,6 +242,12 @@ PATH_NAMES = {0: "none", 1: "matrix_prefill", 2: "matrix_decode", 3: "streaming"
 
 def gqa_last_path() -> int:
     return int(load().gqa_last_path())
+
+
+def gqa_probe_mfma_peak(blocks, iters, stamps, sink, stream) -> int:
+    """Measurement aid (include/gqa_probe.h): back-to-back bf16 MFMAs with
+    shader-clock and 100 MHz stamps per wave."""
+    return load().gqa_probe_mfma_peak(blocks, iters, stamps, sink, stream)
 
 
 def gqa_last_error() -> str:
