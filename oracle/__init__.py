@@ -11,6 +11,7 @@ nothing from the product path.
 ``rotary``     rotary position embedding of Q and of K before it enters the cache.
 ``rolling``    the rolling (ring-buffer) KV cache of a windowed layer.
 ``fp8``        an FP8 (E4M3) KV cache with per-tensor scales.
+``int8``       an INT8 KV cache with per-KV-head scales.
 """
 
 from .materialized import (  # noqa: F401
@@ -26,3 +27,4 @@ from . import brute  # noqa: F401
 from . import rotary  # noqa: F401
 from . import rolling  # noqa: F401
 from . import fp8  # noqa: F401
+from . import int8  # noqa: F401
