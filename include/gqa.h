@@ -372,6 +372,38 @@ gqa_status gqa_decode_fp8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capa
                           float k_scale, float v_scale,
                           void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* INT8 KV cache with per-KV-head scales (the same pages name quantized
+ * caches only as outside their scope; every rule here is this library's
+ * reading).  The caches are int8 [B, Hkv, capacity, D] of symmetric codes in
+ * -127 .. 127 with one fp32 scale per KV head for K and one for V, device
+ * arrays [Hkv] (the same for every batch): K[b, g] = code * k_scales[g].
+ * Strides of the caches are in bytes (= elements), multiples of 16.  The
+ * scales must be finite and > 0 (device memory: not checked).
+ *
+ * gqa_append_kv_int8: gqa_append_kv that quantizes the new rows (the plan's
+ * dtype): code = x * fp32(1 / scale[g]) computed in fp32, rounded to the
+ * nearest integer with ties to even, clamped to +-127; NaN gives 0.
+ * Errors: as gqa_append_kv, and INVALID_ARG for NULL scales. */
+gqa_status gqa_append_kv_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                              gqa_tensor k_new, gqa_tensor v_new,
+                              gqa_tensor k_cache, gqa_tensor v_cache,
+                              const int32_t* seqlens_k, const float* k_scales, const float* v_scales,
+                              void* hip_stream);
+
+/* gqa_decode against INT8 caches (arguments otherwise as gqa_decode).  The
+ * matrix-core split-KV decode streams the codes (half the bytes of a 16-bit
+ * cache), turns each 16-key unit into the plan's 16-bit type in LDS (exact),
+ * folds each KV head's k_scale into the softmax scale and its v_scale into
+ * the normalization.  Needs a bf16 or fp16 plan of head size 64, 128 or 256
+ * (UNSUPPORTED otherwise); no caller mask.
+ * Errors: as gqa_decode, INVALID_ARG for NULL scales, UNSUPPORTED for other
+ *   plans or more than 2048 row tiles. */
+gqa_status gqa_decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                           gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                           const int32_t* seqlens_k, const float* head_sink,
+                           const float* k_scales, const float* v_scales,
+                           void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* gqa_decode_fp8 with a caller mask over [B, Hq, curr, capacity], as for
  * gqa_decode_masked ("Attention Kernel Design", section "Layouts and
  * semantics": boolean or additive attention_bias broadcast over batch and

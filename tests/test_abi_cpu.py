@@ -317,6 +317,27 @@ def test_fp8_validation():
     assert dm(ok, Bn=0) == B.GQA_OK
 
 
+def test_int8_validation():
+    h = plan()
+    s = ctypes.c_void_p(FAKE)
+    ws = B.gqa_workspace_size(h)
+    c8 = B.gqa_tensor(FAKE, 1024 * 128 * 2, 1024 * 128, 128)
+    sc = ctypes.c_void_p(FAKE)
+    def app(ks=sc, Bn=2, kc=c8):
+        return B.gqa_append_kv_int8(h, Bn, 1, 64, t(), t(), kc, c8, s, ks, sc, None)
+    def dec(ks=sc, hh=h, wsp=FAKE, Bn=2):
+        return B.gqa_decode_int8(hh, Bn, 1, 64, t(), c8, c8, t(), s, None, ks, sc,
+                                 ctypes.c_void_p(wsp) if wsp else None, ws, None)
+    assert app(ks=None) == B.GQA_ERR_INVALID_ARG and "scales" in B.gqa_last_error()
+    assert app(kc=B.gqa_tensor(FAKE, 1024 * 128 * 2, 1024 * 128, 100)) == B.GQA_ERR_UNSUPPORTED
+    assert app(Bn=0) == B.GQA_OK
+    assert dec(ks=None) == B.GQA_ERR_INVALID_ARG
+    assert dec(wsp=0) == B.GQA_ERR_INVALID_ARG and "workspace" in B.gqa_last_error()
+    st, hf = B.gqa_plan(attrs(dtype=B.GQA_F32), 4, 16, 1024)
+    assert dec(hh=hf) == B.GQA_ERR_UNSUPPORTED and "INT8" in B.gqa_last_error()
+    assert dec(Bn=0) == B.GQA_OK
+
+
 def test_last_path_is_none_after_failed_or_empty_calls():
     h = plan()
     assert _prefill(h, Lq=17) == B.GQA_ERR_CAPACITY

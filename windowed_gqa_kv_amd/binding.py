@@ -34,7 +34,8 @@ EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
             "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
             "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_append_decode", "gqa_prefill_rotary",
-            "gqa_last_path", "gqa_last_error", "gqa_probe_mfma_peak")
+            "gqa_last_path", "gqa_last_error", "gqa_probe_mfma_peak",
+            "gqa_append_kv_int8", "gqa_decode_int8")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
@@ -130,6 +131,10 @@ def load():
     lib.gqa_append_decode.restype = ctypes.c_int
     lib.gqa_prefill_rotary.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, RT, P]
     lib.gqa_prefill_rotary.restype = ctypes.c_int
+    lib.gqa_append_kv_int8.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P, P]
+    lib.gqa_append_kv_int8.restype = ctypes.c_int
+    lib.gqa_decode_int8.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P, P, P, S, P]
+    lib.gqa_decode_int8.restype = ctypes.c_int
     lib.gqa_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P]
     lib.gqa_probe_mfma_peak.restype = ctypes.c_int
     lib.gqa_last_path.argtypes = []
@@ -242,6 +247,18 @@ PATH_NAMES = {0: "none", 1: "matrix_prefill", 2: "matrix_decode", 3: "streaming"
 
 def gqa_last_path() -> int:
     return int(load().gqa_last_path())
+
+
+def gqa_append_kv_int8(plan, B, curr, capacity, k_new, v_new, k_cache, v_cache, seqlens_k, k_scales, v_scales,
+                       stream) -> int:
+    return load().gqa_append_kv_int8(plan, B, curr, capacity, k_new, v_new, k_cache, v_cache, seqlens_k,
+                                     k_scales, v_scales, stream)
+
+
+def gqa_decode_int8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scales, v_scales,
+                    workspace, ws_bytes, stream) -> int:
+    return load().gqa_decode_int8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink,
+                                  k_scales, v_scales, workspace, ws_bytes, stream)
 
 
 def gqa_probe_mfma_peak(blocks, iters, stamps, sink, stream) -> int:
@@ -636,6 +653,48 @@ class Plan:
         check(gqa_append_kv_fp8(self._h, B, curr, k_cache.shape[2], tensor_view(k_new),
                                 tensor_view(v_new), tensor_view(k_cache), tensor_view(v_cache),
                                 _ptr(seqlens_k), float(k_scale), float(v_scale), _stream(stream)))
+
+    # ---- INT8 KV caches: int8 tensors of codes, per-KV-head scales ----
+    def _int8_args(self, k_cache, v_cache, k_scales, v_scales):
+        import torch
+        if k_cache.dtype != torch.int8 or v_cache.dtype != torch.int8:
+            raise TypeError("INT8 caches are int8 tensors of codes")
+        _aux("k_scales", k_scales, torch.float32, self.kv_num_heads)
+        _aux("v_scales", v_scales, torch.float32, self.kv_num_heads)
+        _need(k_scales is not None and v_scales is not None, "k_scales and v_scales are required")
+
+    def append_kv_int8(self, k_new, v_new, k_cache, v_cache, seqlens_k, k_scales, v_scales, *, stream=None):
+        import torch
+        self._check_dtype(k_new, v_new)
+        self._int8_args(k_cache, v_cache, k_scales, v_scales)
+        B, curr = self._rows("k_new", k_new, self.kv_num_heads)
+        _need(tuple(v_new.shape) == tuple(k_new.shape), "k_new and v_new differ in shape")
+        self._caches(B, k_cache, v_cache)
+        _need(seqlens_k is not None, "seqlens_k is required")
+        _aux("seqlens_k", seqlens_k, torch.int32, B)
+        _same_device(k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, seqlens_k=seqlens_k,
+                     k_scales=k_scales, v_scales=v_scales)
+        check(gqa_append_kv_int8(self._h, B, curr, k_cache.shape[2], tensor_view(k_new), tensor_view(v_new),
+                                 tensor_view(k_cache), tensor_view(v_cache), _ptr(seqlens_k), _ptr(k_scales),
+                                 _ptr(v_scales), _stream(stream)))
+
+    def decode_int8(self, q, k_cache, v_cache, seqlens_k, k_scales, v_scales, out=None, *, head_sink=None,
+                    workspace=None, stream=None):
+        import torch
+        self._check_dtype(q, out)
+        self._int8_args(k_cache, v_cache, k_scales, v_scales)
+        self._decode_args(q, k_cache, v_cache, seqlens_k, out, head_sink, workspace, None, torch.int8)
+        _same_device(q, k_scales=k_scales, v_scales=v_scales)
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.new_workspace(q.device)
+        B, _, curr, _ = q.shape
+        check(gqa_decode_int8(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_cache),
+                              tensor_view(v_cache), tensor_view(out), _ptr(seqlens_k), _ptr(head_sink),
+                              _ptr(k_scales), _ptr(v_scales), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
+        return out
 
     def decode_fp8(self, q, k_cache, v_cache, seqlens_k, k_scale, v_scale, out=None, *,
                    head_sink=None, workspace=None, mask=None, stream=None):

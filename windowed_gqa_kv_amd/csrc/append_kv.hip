@@ -75,8 +75,23 @@ __device__ __forceinline__ uint32_t e4m3_pack4(const float* t) {
   return u;
 }
 
-template <int DT, typename I>
-__global__ __launch_bounds__(256) void append_kv_fp8_kernel(AppendArgs a) {
+// INT8 cache: code = x * r in fp32 (r = fp32(1 / scale[g]), a correctly
+// rounded division), rounded to the nearest integer with ties to even,
+// clamped to +-127; NaN gives 0.
+__device__ __forceinline__ uint32_t i8_pack4(const float* t) {
+  uint32_t u = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float c = t[i] != t[i] ? 0.0f : fminf(fmaxf(__builtin_rintf(t[i]), -127.0f), 127.0f);
+    u |= ((uint32_t)(int)c & 0xffu) << (8 * i);
+  }
+  return u;
+}
+
+// QK = 1: FP8 (E4M3) codes with per-tensor scales; QK = 2: INT8 codes with
+// per-KV-head scales.
+template <int DT, int QK, typename I>
+__global__ __launch_bounds__(256) void append_kv_q8_kernel(AppendArgs a) {
   constexpr int E = DT == kF32 ? 4 : 2;
   const int chunks = a.row_bytes / (8 * E);  // 8-element chunks per row
   const I n = (I)a.B * a.Hkv * a.curr * chunks;
@@ -97,35 +112,47 @@ __global__ __launch_bounds__(256) void append_kv_fp8_kernel(AppendArgs a) {
   if (total < a.curr || (!a.rolling && total > a.capacity)) return;  // out-of-range length: skip batch
   int64_t slot = total - a.curr + t;
   if (a.rolling) slot %= a.capacity;
-  const float rr = is_v ? a.v_rcp : a.k_rcp;
+  const float rr = QK == 1 ? (is_v ? a.v_rcp : a.k_rcp) : 1.0f / (is_v ? a.v_scales : a.k_scales)[g];
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] *= rr;
   char* dst = reinterpret_cast<char*>(is_v ? a.v_cache : a.k_cache);
   const int64_t dof = is_v ? (b * a.vc_sb + g * a.vc_sh + slot * a.vc_ss) : (b * a.kc_sb + g * a.kc_sh + slot * a.kc_ss);
-  *reinterpret_cast<u32x2*>(dst + dof + 8 * c) = u32x2{e4m3_pack4(f), e4m3_pack4(f + 4)};
+  if constexpr (QK == 1)
+    *reinterpret_cast<u32x2*>(dst + dof + 8 * c) = u32x2{e4m3_pack4(f), e4m3_pack4(f + 4)};
+  else
+    *reinterpret_cast<u32x2*>(dst + dof + 8 * c) = u32x2{i8_pack4(f), i8_pack4(f + 4)};
 }
 
-}  // namespace
-
-hipError_t launch_append_kv_fp8(const AppendArgs& a, int dtype, hipStream_t stream) {
+template <int QK>
+hipError_t launch_q8(const AppendArgs& a, int dtype, hipStream_t stream) {
   const int E = dtype == kF32 ? 4 : 2;
   const int64_t n = (int64_t)a.B * a.Hkv * a.curr * (a.row_bytes / (8 * E));
   if (n == 0) return hipSuccess;
   dim3 grid((unsigned)((n + 255) / 256), 2);
   const bool small = n + 255 <= (int64_t)UINT32_MAX;
   if (dtype == kBF16) {
-    if (small) hipLaunchKernelGGL((append_kv_fp8_kernel<kBF16, uint32_t>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((append_kv_fp8_kernel<kBF16, int64_t>), grid, dim3(256), 0, stream, a);
+    if (small) hipLaunchKernelGGL((append_kv_q8_kernel<kBF16, QK, uint32_t>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((append_kv_q8_kernel<kBF16, QK, int64_t>), grid, dim3(256), 0, stream, a);
   } else if (dtype == kF16) {
-    if (small) hipLaunchKernelGGL((append_kv_fp8_kernel<kF16, uint32_t>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((append_kv_fp8_kernel<kF16, int64_t>), grid, dim3(256), 0, stream, a);
+    if (small) hipLaunchKernelGGL((append_kv_q8_kernel<kF16, QK, uint32_t>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((append_kv_q8_kernel<kF16, QK, int64_t>), grid, dim3(256), 0, stream, a);
   } else if (dtype == kF32) {
-    if (small) hipLaunchKernelGGL((append_kv_fp8_kernel<kF32, uint32_t>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((append_kv_fp8_kernel<kF32, int64_t>), grid, dim3(256), 0, stream, a);
+    if (small) hipLaunchKernelGGL((append_kv_q8_kernel<kF32, QK, uint32_t>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((append_kv_q8_kernel<kF32, QK, int64_t>), grid, dim3(256), 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append_kv_fp8(const AppendArgs& a, int dtype, hipStream_t stream) {
+  return launch_q8<1>(a, dtype, stream);
+}
+
+hipError_t launch_append_kv_int8(const AppendArgs& a, int dtype, hipStream_t stream) {
+  return launch_q8<2>(a, dtype, stream);
 }
 
 hipError_t launch_append_kv(const AppendArgs& a, hipStream_t stream) {

@@ -66,8 +66,10 @@ struct AttnArgs {
   // Decode on FP8 (E4M3) caches: k and v hold codes (byte strides), the K
   // scale is folded into scale_log2 / scale_over_cap, the V scale multiplies
   // the normalized output.
-  int32_t kv_fp8;
-  float v_scale;        // 1 unless kv_fp8
+  int32_t kv_fp8;       // 1: FP8 (E4M3) caches; 2: INT8 caches with per-KV-head scales
+  float v_scale;        // 1 unless FP8
+  const float* k_scales;  // INT8: device fp32 [Hkv], folded into the scores per KV head
+  const float* v_scales;  // INT8: device fp32 [Hkv], multiplies the normalized output
   float scale_log2;     // scale * log2(e)
   float scale_over_cap; // scale / softcap (softcap > 0 only)
   float cap_log2;       // softcap * log2(e)

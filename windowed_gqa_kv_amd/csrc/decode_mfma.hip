@@ -362,7 +362,8 @@ __device__ __forceinline__ void merge_tile_q(const AttnArgs& a, int lrp, int R, 
       } else {
         fac = 1.0f / Ls;
       }
-      fac *= a.v_scale;  // an FP8 V cache holds V / v_scale (1 otherwise)
+      // an FP8 V cache holds V / v_scale, an INT8 one V / v_scales[g] (1 otherwise)
+      fac *= a.v_scales != nullptr ? a.v_scales[xg] : a.v_scale;
 #pragma unroll
       for (int q = 0; q < QPL; ++q) store_row4<IS_BF16, D>(a, xb, h, row / a.G, 4 * (c * QPL + q), acc[q] * fac);
     }
@@ -397,9 +398,10 @@ __device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt,
 // [B, Hq, curr, capacity], the key index being the cache slot.  FUSE: the
 // step's append is part of the launch (16-bit caches, no mask); a separate
 // instance, so that the other instances keep their code.
-template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8, bool FUSE = false>
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK, int KVQ, bool FUSE = false>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int nrt,
                                                      float* __restrict__ part, unsigned* __restrict__ counters) {
+  constexpr bool KV8 = KVQ != 0;  // one-byte codes: FP8 (KVQ = 1) or INT8 (KVQ = 2)
   using RG = Ring<D, KV8>;
   using KT = std::conditional_t<KV8, uint8_t, uint16_t>;  // cache element
   constexpr int KQ = D / 32;    // k-steps of 16x16x32 over the head dim
@@ -673,6 +675,11 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     }
     const int c_lo = x.lo + kSub * ua;
     const int c_hi = min(x.hi, x.lo + kSub * ub - 1);
+    // INT8 caches: the KV head's K scale joins the softmax scale (raw scores
+    // are in code units)
+    const float kq = KVQ == 2 ? a.k_scales[x.g] : 1.0f;
+    const float c_l2p = SOFTCAP ? 1.0f : c_l2 * kq;
+    const float soc = a.scale_over_cap * kq;
 
     // this lane's query row (padding rows carry zeros and are never stored)
     const int my_r = kRowsPerTile * x.rt + n;
@@ -849,7 +856,12 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
             uint32_t hw[8];  // two 16-bit values per word, byte order kept
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              if constexpr (IS_BF16) {
+              if constexpr (KVQ == 2) {
+                // INT8 codes (|c| <= 127) are exact in bf16 and fp16
+                const uint32_t cw = raw[q];
+                hw[2 * q] = pack2<IS_BF16>((float)(int8_t)(cw & 0xffu), (float)(int8_t)((cw >> 8) & 0xffu));
+                hw[2 * q + 1] = pack2<IS_BF16>((float)(int8_t)((cw >> 16) & 0xffu), (float)(int8_t)(cw >> 24));
+              } else if constexpr (IS_BF16) {
                 hw[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, false));
                 hw[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, true));
               } else {
@@ -880,7 +892,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
         for (int r = 0; r < 4; ++r) {
           float x = sc[r];
           if constexpr (MASK == 2) x = fmaf(mf_cur[r], a.bias_mul, x);
-          sc[r] = a.cap_log2 * tanh_f32(x * a.scale_over_cap);
+          sc[r] = a.cap_log2 * tanh_f32(x * soc);
         }
       }
       const bool interior = (a.window < 0 || kb >= p_last - a.window + 1) &&
@@ -906,9 +918,9 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       bm = fmaxf(bm, xor16(bm));
       bm = fmaxf(bm, xor32(bm));
       const float m_new = fmaxf(m_run, bm);
-      const bool need = (m_new - m_run) * c_l2 > kRescaleLog2;
+      const bool need = (m_new - m_run) * c_l2p > kRescaleLog2;
       if (__any(need)) {
-        const float alpha = need ? fast_exp2((m_run - m_new) * c_l2) : 1.0f;
+        const float alpha = need ? fast_exp2((m_run - m_new) * c_l2p) : 1.0f;
         m_run = need ? m_new : m_run;
         l_run *= alpha;
 #pragma unroll
@@ -916,11 +928,11 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[db][r] *= alpha;
       }
-      const float mb = m_run == -INFINITY ? 0.0f : m_run * c_l2;
+      const float mb = m_run == -INFINITY ? 0.0f : m_run * c_l2p;
       float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[r] = fast_exp2(fmaf(sc[r], c_l2, -mb));
+        pv[r] = fast_exp2(fmaf(sc[r], c_l2p, -mb));
         l_run += pv[r];
       }
       const u32x2 pp = u32x2{pack2<IS_BF16>(pv[0], pv[1]), pack2<IS_BF16>(pv[2], pv[3])};
@@ -953,8 +965,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       const float l_b = ml[(D / 4 + 1) * 64 + lane];
       const float M = fmaxf(m_run, m_b);
       if (M == -INFINITY) return;
-      const float fa = fast_exp2((m_run - M) * c_l2);
-      const float fb = fast_exp2((m_b - M) * c_l2);
+      const float fa = fast_exp2((m_run - M) * c_l2p);
+      const float fb = fast_exp2((m_b - M) * c_l2p);
       l_run = l_run * fa + l_b * fb;
       m_run = M;
 #pragma unroll
@@ -980,7 +992,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
 #pragma unroll
           for (int r = 0; r < 4; ++r) coherent_store(p + n * D + 16 * db + 4 * q4 + r, o[db][r]);
         if (q4 == 0) {
-          coherent_store(p + kRowsPerTile * D + n, m_run == -INFINITY ? -INFINITY : m_run * c_l2);
+          coherent_store(p + kRowsPerTile * D + n, m_run == -INFINITY ? -INFINITY : m_run * c_l2p);
           coherent_store(p + kRowsPerTile * D + kRowsPerTile + n, l_row);
         }
       }
@@ -1044,13 +1056,13 @@ int resident_grid(K kernel) {
 
 // The grid of one kernel instance on the current device (computed once per
 // device; a benign race computes the same value).
-template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8, bool FUSE>
+template <bool IS_BF16, int D, bool SOFTCAP, int MASK, int KVQ, bool FUSE>
 int grid_of() {
   static int grid_cache[16] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   int G = grid_cache[dev];
-  if (G == 0) G = grid_cache[dev] = resident_grid(decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8, FUSE>);
+  if (G == 0) G = grid_cache[dev] = resident_grid(decode_kernel<IS_BF16, D, SOFTCAP, MASK, KVQ, FUSE>);
   return G;
 }
 
@@ -1058,20 +1070,22 @@ int grid_of() {
 template <bool IS_BF16, int D, typename Op>
 auto visit_d(const AttnArgs& a, bool softcap, const Op& op) {
   if (a.fuse_append)  // 16-bit caches, no mask (the host guarantees both)
-    return softcap ? op.template run<IS_BF16, D, true, 0, false, true>()
-                   : op.template run<IS_BF16, D, false, 0, false, true>();
+    return softcap ? op.template run<IS_BF16, D, true, 0, 0, true>()
+                   : op.template run<IS_BF16, D, false, 0, 0, true>();
+  if (a.kv_fp8 == 2)  // INT8 caches, no mask (the host guarantees it)
+    return softcap ? op.template run<IS_BF16, D, true, 0, 2>() : op.template run<IS_BF16, D, false, 0, 2>();
   if (a.kv_fp8) {
     if (a.mask_kind == 1)
-      return softcap ? op.template run<IS_BF16, D, true, 1, true>() : op.template run<IS_BF16, D, false, 1, true>();
+      return softcap ? op.template run<IS_BF16, D, true, 1, 1>() : op.template run<IS_BF16, D, false, 1, 1>();
     if (a.mask_kind == 2)
-      return softcap ? op.template run<IS_BF16, D, true, 2, true>() : op.template run<IS_BF16, D, false, 2, true>();
-    return softcap ? op.template run<IS_BF16, D, true, 0, true>() : op.template run<IS_BF16, D, false, 0, true>();
+      return softcap ? op.template run<IS_BF16, D, true, 2, 1>() : op.template run<IS_BF16, D, false, 2, 1>();
+    return softcap ? op.template run<IS_BF16, D, true, 0, 1>() : op.template run<IS_BF16, D, false, 0, 1>();
   }
   if (a.mask_kind == 1)
-    return softcap ? op.template run<IS_BF16, D, true, 1, false>() : op.template run<IS_BF16, D, false, 1, false>();
+    return softcap ? op.template run<IS_BF16, D, true, 1, 0>() : op.template run<IS_BF16, D, false, 1, 0>();
   if (a.mask_kind == 2)
-    return softcap ? op.template run<IS_BF16, D, true, 2, false>() : op.template run<IS_BF16, D, false, 2, false>();
-  return softcap ? op.template run<IS_BF16, D, true, 0, false>() : op.template run<IS_BF16, D, false, 0, false>();
+    return softcap ? op.template run<IS_BF16, D, true, 2, 0>() : op.template run<IS_BF16, D, false, 2, 0>();
+  return softcap ? op.template run<IS_BF16, D, true, 0, 0>() : op.template run<IS_BF16, D, false, 0, 0>();
 }
 template <typename Op, typename R>
 R visit(const AttnArgs& a, int dtype, bool softcap, const Op& op, R unsupported) {
@@ -1092,20 +1106,20 @@ struct LaunchOp {
   const DecodeGeometry& geo;
   float* ws;
   hipStream_t stream;
-  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8, bool FUSE = false>
+  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, int KVQ, bool FUSE = false>
   hipError_t run() const {
-    const int G = grid_of<IS_BF16, D, SOFTCAP, MASK, KV8, FUSE>();
+    const int G = grid_of<IS_BF16, D, SOFTCAP, MASK, KVQ, FUSE>();
     unsigned* counters = reinterpret_cast<unsigned*>(ws);
     float* part = ws + geo.counter_floats;
-    hipLaunchKernelGGL((decode_kernel<IS_BF16, D, SOFTCAP, MASK, KV8, FUSE>), dim3(G), dim3(256), 0, stream, a,
+    hipLaunchKernelGGL((decode_kernel<IS_BF16, D, SOFTCAP, MASK, KVQ, FUSE>), dim3(G), dim3(256), 0, stream, a,
                        geo.rows, geo.row_tiles, part, counters);
     return hipGetLastError();
   }
 };
 struct GridOp {
-  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, bool KV8, bool FUSE = false>
+  template <bool IS_BF16, int D, bool SOFTCAP, int MASK, int KVQ, bool FUSE = false>
   int run() const {
-    return grid_of<IS_BF16, D, SOFTCAP, MASK, KV8, FUSE>();
+    return grid_of<IS_BF16, D, SOFTCAP, MASK, KVQ, FUSE>();
   }
 };
 

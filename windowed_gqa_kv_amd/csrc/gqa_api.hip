@@ -879,6 +879,85 @@ GQA_API gqa_status gqa_decode_fp8_masked(gqa_plan_t plan, int32_t B, int32_t cur
                     mask, workspace, ws_bytes, hip_stream);
 }
 
+GQA_API gqa_status gqa_append_kv_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                      gqa_tensor k_new, gqa_tensor v_new, gqa_tensor k_cache,
+                                      gqa_tensor v_cache, const int32_t* seqlens_k, const float* k_scales,
+                                      const float* v_scales, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (curr > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the plan's max_q_len %d", curr, plan->max_q_len);
+  if (capacity > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
+                (long long)plan->max_kv_len);
+  if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  if (k_scales == nullptr || v_scales == nullptr) return fail(GQA_ERR_INVALID_ARG, "k_scales and v_scales are required");
+  gqa_status st = check_ring(plan, curr, capacity);
+  if (st != GQA_OK) return st;
+  if (B == 0 || curr == 0) return GQA_OK;
+  if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("k_new", k_new, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("v_new", v_new, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, 1)) != GQA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, 1)) != GQA_OK) return st;
+  gqa::AppendArgs a = append_args(plan, B, curr, capacity, k_new, v_new, k_cache, v_cache, seqlens_k);
+  // code caches: strides are bytes already
+  a.kc_sb = k_cache.stride_b; a.kc_sh = k_cache.stride_h; a.kc_ss = k_cache.stride_s;
+  a.vc_sb = v_cache.stride_b; a.vc_sh = v_cache.stride_h; a.vc_ss = v_cache.stride_s;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  return hip_status(gqa::launch_append_kv_int8(a, (int)plan->attrs.dtype, reinterpret_cast<hipStream_t>(hip_stream)),
+                    "append_kv_int8 launch");
+}
+
+GQA_API gqa_status gqa_decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                                   gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                   const int32_t* seqlens_k, const float* head_sink, const float* k_scales,
+                                   const float* v_scales, void* workspace, size_t ws_bytes, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
+  if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
+  if (curr > plan->max_q_len)
+    return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the plan's max_q_len %d", curr, plan->max_q_len);
+  if (capacity > plan->max_kv_len)
+    return fail(GQA_ERR_CAPACITY, "capacity = %lld exceeds the plan's max_kv_len %lld", (long long)capacity,
+                (long long)plan->max_kv_len);
+  if (curr > capacity) return fail(GQA_ERR_CAPACITY, "curr = %d exceeds the cache capacity %lld", curr, (long long)capacity);
+  gqa_status st = check_fp8_plan(plan);
+  if (st != GQA_OK) return fail(GQA_ERR_UNSUPPORTED, "INT8 caches need a bf16 or fp16 plan of head size 64, 128 or 256");
+  if (k_scales == nullptr || v_scales == nullptr) return fail(GQA_ERR_INVALID_ARG, "k_scales and v_scales are required");
+  if ((st = check_sink(plan, head_sink)) != GQA_OK) return st;
+  if ((st = check_ring(plan, curr, capacity)) != GQA_OK) return st;
+  if (B == 0 || curr == 0) return GQA_OK;
+  if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const int esz = elem_size(plan->attrs.dtype);
+  if ((st = check_tensor("q", q, esz)) != GQA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, 1)) != GQA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, 1)) != GQA_OK) return st;
+  if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
+  gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
+  a.seqlens = seqlens_k;
+  a.head_sink = head_sink;
+  a.kv_fp8 = 2;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
+  const size_t need = geo.ws_floats * sizeof(float);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(GQA_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
+                workspace ? "" : ", NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (!geo.fits) return fail(GQA_ERR_UNSUPPORTED, "INT8 caches: at most %d row tiles per call", gqa::kDecodeMaxTiles);
+  return hip_status(path_decode_mfma(a, (int)plan->attrs.dtype, plan->attrs.softcap > 0, geo,
+                                     reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(hip_stream)),
+                    "decode_int8 launch");
+}
+
 GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }
 
 GQA_API gqa_path gqa_last_path(void) { return (gqa_path)g_path; }

@@ -60,11 +60,15 @@ struct AppendArgs {
   int32_t capacity;
   int32_t rolling;  // 1: slot = position mod capacity, positions may pass it
   float k_rcp, v_rcp;  // FP8 caches: fp32(1 / scale) of K and V
+  const float* k_scales;  // INT8 caches: per-KV-head scales of K and V (device fp32 [Hkv])
+  const float* v_scales;
 };
 hipError_t launch_append_kv(const AppendArgs& a, hipStream_t stream);
 // The same into FP8 (E4M3) caches (byte strides for the caches, element
 // strides times the element size for the new rows; row_bytes of the new rows).
 hipError_t launch_append_kv_fp8(const AppendArgs& a, int dtype, hipStream_t stream);
+// The same into INT8 caches with per-KV-head scales (a.k_scales / a.v_scales).
+hipError_t launch_append_kv_int8(const AppendArgs& a, int dtype, hipStream_t stream);
 
 // Rotary position embedding: up to three jobs in one launch (blockIdx.y),
 // each turning (turn = 1) or copying (turn = 0) rows [B, H[j], L, D] of
