@@ -29,7 +29,8 @@ speculative-decode workload against a rolling cache of W + curr - 1 slots;
 `masks` times the long prompt through the masked matrix-core prefill with an
 all-True and block-sparse boolean masks (16x64 and 128x64 blocks), an
 additive one and one with softcap, beside the unmasked prefill; `fp8` times
-the headline decode on FP8 (E4M3) caches; `peaks_measured` reports the dense
+the headline decode on FP8 (E4M3) caches, and on INT8 caches with per-KV-head
+scales; `peaks_measured` reports the dense
 bf16 MFMA rate and shader clock measured on the device and a 1 GiB copy's
 rate, for context (fractions stay against the published peaks).
 
@@ -549,12 +550,40 @@ def bench_fp8(reps):
         times.append(sum(a.elapsed_time(b) for a, b in ev) / (reps * R))
         del g
     ms, ms_masked = times
+    del caches
+    # the same decode on INT8 caches with per-KV-head scales
+    ksc = torch.full((w.Hkv,), 0.03, device="cuda")
+    ic0 = torch.clamp(torch.round(d["k_cache"].float() / 0.03), -127, 127).to(torch.int8).cuda()
+    iv0 = torch.clamp(torch.round(d["v_cache"].float() / 0.03), -127, 127).to(torch.int8).cuda()
+    icaches = [(ic0.clone(), iv0.clone()) for _ in range(R)]
+    del ic0, iv0
+    for kc, vc in icaches:
+        plan.append_kv_int8(kn, vn, kc, vc, seq, ksc, ksc)
+        plan.decode_int8(q, kc, vc, seq, ksc, ksc, out, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for kc, vc in icaches:
+            plan.decode_int8(q, kc, vc, seq, ksc, ksc, out, workspace=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = _events(reps)
+    for a, b_ in ev:
+        a.record()
+        g.replay()
+        b_.record()
+    torch.cuda.synchronize()
+    ms_i8 = sum(a.elapsed_time(b_) for a, b_ in ev) / (reps * R)
+    del g, icaches
     s = d["seqlens_k"].numpy().astype("int64")
     b = work.decode_bytes(s, w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window, kv_dtype="fp8")
     return {"workload": w.name, "kernel": "decode_kernel (FP8 caches)", "kernel_ms": round(ms, 5),
             "bytes_per_launch": b, "achieved": round(b / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
             "frac": round(b / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-            "bool_mask_kernel_ms": round(ms_masked, 5)}
+            "bool_mask_kernel_ms": round(ms_masked, 5),
+            "int8": {"kernel": "decode_kernel (INT8 caches, per-KV-head scales)", "kernel_ms": round(ms_i8, 5),
+                     "bytes_per_launch": b, "achieved": round(b / (ms_i8 / 1e3) / 1e9, 2),
+                     "frac": round(b / (ms_i8 / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}}
 
 
 def peaks_measured():
