@@ -310,7 +310,7 @@ typedef struct {
 } gqa_mask;
 
 /* gqa_prefill with a caller mask (arguments otherwise as gqa_prefill).  On a
- * bf16 or fp16 plan of head size 64 or 128 (with or without softcap), a boolean mask
+ * bf16 or fp16 plan of head size 32, 64, 128 or 256 (with or without softcap), a boolean mask
  * whose data and strides are multiples of 8 bytes, or an additive one whose
  * data is 16-byte aligned and strides multiples of 4 elements, runs on the
  * matrix-core prefill: each wave reads its rows' entries of a 64-key tile (a

@@ -61,7 +61,7 @@ def _scales(Hkv, seed, lo, hi):
     return torch.from_numpy(np.random.default_rng(seed).uniform(lo, hi, Hkv).astype(np.float32))
 
 
-def _run(w, d, ks, vs, rolling=False):
+def _run(w, d, ks, vs):
     rng = np.random.default_rng(w.seed)
     kc0 = torch.from_numpy(rng.integers(-127, 128, (w.B, w.Hkv, w.Lk, w.D)).astype(np.int8))
     vc0 = torch.from_numpy(rng.integers(-127, 128, (w.B, w.Hkv, w.Lk, w.D)).astype(np.int8))
@@ -154,3 +154,34 @@ def test_int8_decode_lazy_rescale(gpu):
     want = oracle.int8.decode(qd, kc_o[:, :, :top], vc_o[:, :, :top], s, k_scales=ks.numpy(),
                               v_scales=vs.numpy(), scale=w.sm_scale, smooth_softmax=True)
     compare(out, want, "bf16", "int8 rescale")
+
+
+def test_int8_decode_rolling(gpu):
+    """A rolling INT8 cache (window 600, three new tokens, a ring of
+    W + curr - 1 = 602 slots, positions far past it, different scales per KV
+    head): the ring after the step equals the oracle's bit for bit, and the
+    decode matches the oracle's attention over the dequantized ring."""
+    W, curr = 600, 3
+    w = Workload("i8ring", "decode", "bf16", B=2, Hq=8, Hkv=2, D=256, Lq=curr, Lk=W + curr - 1, window=W,
+                 softcap=30.0, head_sink=True, seqlens=("list", [5000, 1300]), seed=831)
+    d = generate(w)
+    rng = np.random.default_rng(832)
+    kc0 = torch.from_numpy(rng.integers(-127, 128, (w.B, w.Hkv, w.Lk, w.D)).astype(np.int8))
+    vc0 = torch.from_numpy(rng.integers(-127, 128, (w.B, w.Hkv, w.Lk, w.D)).astype(np.int8))
+    ks, vs = _scales(w.Hkv, 833, 0.02, 0.06), _scales(w.Hkv, 834, 0.01, 0.05)
+    plan = make_plan(w, rolling_cache=True)
+    kc, vc = kc0.cuda(), vc0.cuda()
+    seq_d = d["seqlens_k"].cuda()
+    plan.append_kv_int8(d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, seq_d, ks.cuda(), vs.cuda())
+    out = plan.decode_int8(d["q"].cuda(), kc, vc, seq_d, ks.cuda(), vs.cuda(), head_sink=d["head_sink"].cuda())
+    torch.cuda.synchronize()
+    s = d["seqlens_k"].numpy().astype(np.int64)
+    kq = oracle.int8.quantize(to_f64(d["k_new"]), ks.numpy()).astype(np.float64)
+    vq = oracle.int8.quantize(to_f64(d["v_new"]), vs.numpy()).astype(np.float64)
+    kr, vr = oracle.rolling.append(kc0.numpy().astype(np.float64), vc0.numpy().astype(np.float64), kq, vq, s)
+    assert np.array_equal(kc.cpu().numpy(), kr.astype(np.int8))
+    assert np.array_equal(vc.cpu().numpy(), vr.astype(np.int8))
+    want = oracle.rolling.decode(to_f64(d["q"]), oracle.int8.dequantize(kr.astype(np.int8), ks.numpy()),
+                                 oracle.int8.dequantize(vr.astype(np.int8), vs.numpy()), s, scale=w.sm_scale,
+                                 window=W, softcap=30.0, head_sink=to_f64(d["head_sink"]))
+    compare(out, want, "bf16", "rolling int8 decode")
