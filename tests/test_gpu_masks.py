@@ -66,6 +66,9 @@ PREFILL = [
     ("f16", 2, 16, 4, 64, 384, 896, -1, 20.0, False, (896, 500), "sparse128", "11"),
     ("bf16", 1, 16, 8, 256, 256, 768, -1, 0.0, False, None, "sparse128", "11"),
     ("f32", 1, 4, 2, 32, 64, 64, 16, 0.0, True, None, "bool", "11"),
+    # rows of more than 2048 key tiles: the tiles past the prefill's tile map
+    # are taken as needed and read byte by byte; the last tile crosses Lk
+    ("bf16", 1, 4, 2, 64, 64, 140008, -1, 0.0, False, None, "sparse128", "11"),
     ("bf16", 1, 8, 2, 128, 300, 300, -1, 0.0, False, None, "sparse", "11"),
     ("f32", 2, 4, 2, 64, 70, 90, 20, 5.0, False, (90, 33), "add", "b1"),
 ]

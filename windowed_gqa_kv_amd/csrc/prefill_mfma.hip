@@ -327,15 +327,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
       }
     }
   };
-  // mk_cur: this tile's runs; mk_nxt: the next tile's; mk_nn: the one after,
-  // loaded two tiles ahead so that the workgroup can vote on a tile before
-  // its DMA would be issued.
-  uint64_t mk_cur[4] = {0, 0, 0, 0}, mk_nxt[4] = {0, 0, 0, 0}, mk_nn[4] = {0, 0, 0, 0};
-  // Whether any wave needs a tile (its band reaches the tile and the mask
-  // leaves one of its rows a key there): one flag per wave and tile parity.
-  // A tile no wave needs is neither loaded nor computed.
-  __shared__ int wg_need[2][kWaves];
+  // mk_cur: this tile's runs; mk_nxt: those of the next tile computed, loaded
+  // one computed tile ahead (only for tiles the mask does not keep whole).
+  uint64_t mk_cur[4] = {0, 0, 0, 0}, mk_nxt[4] = {0, 0, 0, 0};
   bool mk_full = false;  // the current tile's mask keeps every key of this wave's rows
+  // Tile maps of the boolean mask, filled by a first pass over the mask
+  // before any K/V is loaded: bit t of need_map is set when some wave of the
+  // workgroup needs tile t (its band reaches the tile and the mask leaves one
+  // of its rows a key there), bit t of full_map[w] when the mask keeps every
+  // key of tile t for wave w's rows.  A tile no wave needs is neither loaded
+  // nor computed, and a tile kept whole reads no mask in the main loop.
+  // Tiles past the map (rows of more than 2048 tiles) are taken as needed and
+  // not whole.
+  constexpr int kMapWords = MASK == 1 ? 64 : 1;
+  __shared__ uint32_t need_map[kMapWords];
+  __shared__ uint32_t full_map[kWaves][kMapWords];
+  const int mapped = MASK == 1 ? min(nblk, 32 * kMapWords) : 0;
+  auto full_at = [&](int t) -> bool {
+    return t < mapped && ((full_map[w][t >> 5] >> (t & 31)) & 1u) != 0;
+  };
   // Additive mask: the same runs as fp32 (two aligned 16-byte loads each),
   // loaded at the start of the tile that uses them: the K Q^T MFMAs cover the
   // latency, and every tile is evaluated in full.  bias / scale in raw score
@@ -550,25 +560,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
 
   // ---- schedule: per tile, K Q^T (the next tile's loads riding along), the
   // softmax, P V; then wait for the next tile and meet ----
-  // a wave's need of the tile at kb (wave-uniform)
-  auto wave_needs = [&](int kb, const uint64_t (&mk)[4]) -> int {
-    bool b0, b1;
-    active(kb, b0, b1);
-    const bool n0 = __any((mk[0] | mk[1]) != 0), n1 = __any((mk[2] | mk[3]) != 0);
-    return (b0 && n0) || (b1 && n1);
-  };
-  if (nblk > 0) dma_tile(kv_lo, 0);
-  if constexpr (MASK == 1) {
-    if (nblk > 0) mask_load(kv_lo, mk_nxt);
-    if (nblk > 1) mask_load(kv_lo + BN, mk_nn);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // Q registers, the first tile (and its mask)
-  if constexpr (MASK == 1) {
-    if (nblk > 1) {
-      const int nd = wave_needs(kv_lo + BN, mk_nn);
-      if (lane == 0) wg_need[1][w] = nd;
+  // the first tile at or after t that the workgroup computes (nblk if none)
+  auto next_tile = [&](int t) -> int {
+    if constexpr (MASK == 1) {
+      while (t < mapped) {
+        const uint32_t word = need_map[t >> 5] >> (t & 31);
+        if (word != 0) return t + __builtin_ctz(word);
+        t = min((t | 31) + 1, mapped);
+      }
     }
+    return min(t, nblk);
+  };
+  if constexpr (MASK == 1) {
+    // ---- the first pass over the boolean mask: fill the tile maps ----
+    // When the mask does not vary over heads, the waves that share their
+    // rows (the hw heads of one row group) split the tiles and each writes
+    // the bits of the whole group, so the workgroup reads each mask byte once.
+    for (int i = tid; i < kMapWords; i += 256) need_map[i] = 0;
+    for (int i = tid; i < kWaves * kMapWords; i += 256) (&full_map[0][0])[i] = 0;
+    __syncthreads();
+    const bool shared_rows = a.m_sh == 0;
+    const int step = shared_rows ? hw : 1;
+    const int g0 = shared_rows ? w - w % hw : w;
+    constexpr int PB = 4;  // tiles in flight per wave (more made no run faster)
+    for (int t0 = shared_rows ? w % hw : 0; t0 < mapped; t0 += PB * step) {
+      // A tile that reaches past Lk is taken as needed (if the band reaches
+      // it) and not whole, without reading it: the main loop reads its runs
+      // byte by byte.
+      uint64_t mk[PB][4];
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        const int kbp = kv_lo + (t0 + p * step) * BN;
+        if (t0 + p * step < mapped && kbp + BN <= a.Lk)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) mk[p][x] = *(global_u64*)(mrow + kbp + 16 * x + 8 * h2);
+      }
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        const int t = t0 + p * step;
+        if (t < mapped) {
+          const int kbp = kv_lo + t * BN;
+          bool b0, b1;
+          active(kbp, b0, b1);
+          bool need = b0 || b1, full = false;
+          if (kbp + BN <= a.Lk) {
+            const bool n0 = __any((mk[p][0] | mk[p][1]) != 0), n1 = __any((mk[p][2] | mk[p][3]) != 0);
+            need = (b0 && n0) || (b1 && n1);
+            // every byte of every run nonzero in every lane (the
+            // has-zero-byte bit trick on each run): the tile keeps all keys
+            constexpr uint64_t kOnes = 0x0101010101010101ull, kHigh = 0x8080808080808080ull;
+            uint64_t zero = 0;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) zero |= (mk[p][x] - kOnes) & ~mk[p][x] & kHigh;
+            full = __all(zero == 0);
+          }
+          const uint32_t bit = 1u << (t & 31);
+          if (lane == 0) {
+            if (need) atomicOr(&need_map[t >> 5], bit);
+            if (full)
+              for (int j = 0; j < step; ++j) atomicOr(&full_map[g0 + j][t >> 5], bit);
+          }
+        }
+      }
+    }
+    __syncthreads();
   }
+  const int t_first = next_tile(0);
+  if (t_first < nblk) dma_tile(kv_lo + t_first * BN, 0);
+  if constexpr (MASK == 1)
+    if (t_first < nblk && !full_at(t_first)) mask_load(kv_lo + t_first * BN, mk_nxt);
+  __builtin_amdgcn_s_waitcnt(0);  // Q registers, the first tile (and its mask)
   tile_barrier();
   if (rot && my_row < a.Lq && my_p >= 0) {
 #pragma unroll
@@ -595,42 +656,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
   u32x4 pb[2][2];
   // One tile; its stage (it & 1) is a compile-time constant, so that every
   // LDS address of the tile is a per-lane register plus an immediate.
-  auto tile = [&](int it, auto stage_tag) {
+  auto tile = [&](int t, int tn, auto stage_tag) {
     constexpr int ST = decltype(stage_tag)::value;
-    const int kb = kv_lo + it * BN;
+    const int kb = kv_lo + t * BN;
+    const int kbn = kv_lo + tn * BN;  // the next tile computed
     // The next tile's loads are spread over the K operand batches (or issued
     // at once by a wave with nothing to compute here): a wave that issued all
     // of them back to back would stall behind the other waves' loads.
-    const bool next = it + 1 < nblk;
-    bool load_next = next;
+    const bool load_next = tn < nblk;
     bool a0, a1;
     active(kb, a0, a1);
     if constexpr (MASK == 1) {
-      // the workgroup's vote on the next tile (flags written before the last
-      // barrier); this tile's runs landed with an earlier tile's loads; fetch
-      // the runs two tiles ahead, and skip sub-tiles whose keys the mask
+      // this tile's runs landed with the previous tile's loads (none if the
+      // mask keeps it whole); fetch those of the next tile computed unless
+      // the mask keeps that one whole; skip sub-tiles whose keys the mask
       // clears for all 32 rows
-      if (next)
-        load_next = (wg_need[(it + 1) & 1][0] | wg_need[(it + 1) & 1][1] | wg_need[(it + 1) & 1][2] |
-                     wg_need[(it + 1) & 1][3]) != 0;
+      mk_full = full_at(t);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        mk_cur[x] = mk_nxt[x];
-        mk_nxt[x] = mk_nn[x];
+      for (int x = 0; x < 4; ++x) mk_cur[x] = mk_nxt[x];
+      if (load_next && !full_at(tn)) mask_load(kbn, mk_nxt);
+      if (!mk_full) {
+        a0 = a0 && __any((mk_cur[0] | mk_cur[1]) != 0);
+        a1 = a1 && __any((mk_cur[2] | mk_cur[3]) != 0);
       }
-      if (it + 2 < nblk) mask_load(kb + 2 * BN, mk_nn);
-      a0 = a0 && __any((mk_cur[0] | mk_cur[1]) != 0);
-      a1 = a1 && __any((mk_cur[2] | mk_cur[3]) != 0);
-      // every byte of every run nonzero (no zero byte: the has-zero-byte bit
-      // trick on each run) in every lane: the tile keeps all its keys
-      constexpr uint64_t kOnes = 0x0101010101010101ull, kHigh = 0x8080808080808080ull;
-      uint64_t zero = 0;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) zero |= (mk_cur[x] - kOnes) & ~mk_cur[x] & kHigh;
-      mk_full = __all(zero == 0);
     }
     auto dma_at = [&](int i) {
-      if (load_next) dma_part(kb + BN, ST ^ 1, i);
+      if (load_next) dma_part(kbn, ST ^ 1, i);
     };
     if constexpr (MASK == 2)
       if (a0 || a1) bias_load(kb);
@@ -642,23 +693,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
       for (int q = 0; q < 4; ++q) softmax_exp(sc[q >> 1], q & 1, pb[q >> 1][q & 1]);
       pv(stage_tag, pb, [] {}, [](int) {});
     } else if (load_next) {
-      dma_tile(kb + BN, ST ^ 1);
+      dma_tile(kbn, ST ^ 1);
     }
     // this wave's loads of the next tile have landed; after the barrier every
     // wave's have, and nobody reads this tile's stage any more
     wait_vm<0>();
-    if constexpr (MASK == 1) {
-      // this wave's need of the tile after next, for the vote at its start
-      if (it + 2 < nblk) {
-        const int nd = wave_needs(kb + 2 * BN, mk_nn);
-        if (lane == 0) wg_need[it & 1][w] = nd;
-      }
-    }
     tile_barrier();
   };
-  for (int it = 0; it < nblk; it += 2) {
-    tile(it, std::integral_constant<int, 0>{});
-    if (it + 1 < nblk) tile(it + 1, std::integral_constant<int, 1>{});
+  if constexpr (MASK == 1) {
+    // from needed tile to needed tile
+    for (int t = t_first; t < nblk;) {
+      int tn = next_tile(t + 1);
+      tile(t, tn, std::integral_constant<int, 0>{});
+      t = tn;
+      if (t >= nblk) break;
+      tn = next_tile(t + 1);
+      tile(t, tn, std::integral_constant<int, 1>{});
+      t = tn;
+    }
+  } else {
+    for (int it = 0; it < nblk; it += 2) {
+      tile(it, it + 1, std::integral_constant<int, 0>{});
+      if (it + 1 < nblk) tile(it + 1, it + 2, std::integral_constant<int, 1>{});
+    }
   }
 
   // ---- epilogue: fold the sink, normalize, narrow, store ----
