@@ -150,6 +150,16 @@ __device__ __forceinline__ float tanh_f32(float y) {
   return copysignf(r, y);
 }
 
+// tanh for the matrix-core kernels, whose scores go on to 16-bit P: with
+// t = e^{-2|y|} (no overflow), tanh|y| = (1 - t) / (1 + t), where 1 - t is
+// exact for t >= 1/2, so small |y| keep their relative accuracy; the hardware
+// reciprocal (about 1 ulp) replaces the division.  Absolute error a few 1e-7,
+// branch-free.
+__device__ __forceinline__ float tanh_fast(float y) {
+  const float t = fast_exp2(-2.0f * kLog2e * fabsf(y));
+  return copysignf((1.0f - t) * fast_rcp(1.0f + t), y);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }

@@ -915,7 +915,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
         for (int r = 0; r < 4; ++r) {
           float x = sc[r];
           if constexpr (MASK == 2) x = fmaf(mf_cur[r], a.bias_mul, x);
-          sc[r] = a.cap_log2 * tanh_f32(x * soc);
+          sc[r] = a.cap_log2 * tanh_fast(x * soc);
         }
       }
       const bool interior = (a.window < 0 || kb >= p_last - a.window + 1) &&

@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
         for (int r2 = 0; r2 < 16; ++r2) {
           float x = acc[r2];
           if constexpr (MASK == 2) x = fmaf(bias[2 * sub + (r2 >> 3)][(r2 >> 2) & 1][r2 & 3], a.bias_mul, x);
-          acc[r2] = a.cap_log2 * tanh_f32(x * a.scale_over_cap);
+          acc[r2] = a.cap_log2 * tanh_fast(x * a.scale_over_cap);
         }
       }
       // masks only where the sub-tile crosses a frontier of some row of this
@@ -652,6 +652,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
     }
   }
 
+  if constexpr (D >= 256) {
+    // One wave per SIMD: Q lives in accumulation registers (the MFMA reads
+    // its operands from them), which leaves the vector registers to the K and
+    // V operands and the softmax instead of spilling them there.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qf[ks]));
+  }
   f32x16 sc[2];
   u32x4 pb[2][2];
   // One tile; its stage (it & 1) is a compile-time constant, so that every
