@@ -187,6 +187,18 @@ __device__ __forceinline__ f32x4 mma_pv(u32x2 a, u32x2 b, f32x4 c) {
 __device__ __forceinline__ void coherent_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Four consecutive floats at byte offset `off` of a partial with the cache
+// policy of the device-scope store above (SC1), 16 bytes wide: a lane's four
+// accumulators of a 16-column block are contiguous, so the 16 lanes of a row
+// write whole 64-byte lines in one instruction instead of a quarter line in
+// each of four.  A raw buffer store over the partial's bytes (out-of-range
+// offsets are dropped by the hardware), which the compiler tracks like any
+// other store; the writers' vmcnt(0) before their arrivals waits for it.
+constexpr int kCpolSC1 = 16;                  // cache-policy bit SC1 (device scope) on gfx94x/gfx950
+constexpr int kRawBufferWord3 = 0x00020000;   // raw (untyped) buffer resource, gfx9 data format field
+__device__ __forceinline__ void coherent_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolSC1);
+}
 
 // A row tile and the union of its rows' allowed intervals.
 struct Tile {
@@ -1010,10 +1022,9 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       l_row += xor32(l_row);
       if (row_ok) {
         float* p = part + (int64_t)(k + t) * PART;  // slot k + t: unique per piece
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(p, 0, PART * 4, kRawBufferWord3);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) coherent_store(p + n * D + 16 * db + 4 * q4 + r, o[db][r]);
+        for (int db = 0; db < DB; ++db) coherent_store4(pr, 4 * (n * D + 16 * db + 4 * q4), o[db]);
         if (q4 == 0) {
           coherent_store(p + kRowsPerTile * D + n, m_run == -INFINITY ? -INFINITY : m_run * c_l2p);
           coherent_store(p + kRowsPerTile * D + kRowsPerTile + n, l_row);
