@@ -176,7 +176,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
   constexpr int DB = D / 32;    // 32-wide output blocks
   constexpr int CPR = D / 8;    // 16-byte chunks per K row
   constexpr int TILE = BN * D;  // elements of one K (or V) tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds[NSTAGE][2 * TILE];
+  // K tiles of both stages, then V tiles of both stages: every operand read of
+  // either stage is a per-lane base register plus an immediate below 64 KB
+  // (with K and V interleaved per stage, stage 1 of head size 256 starts
+  // 64 KB in, past the offset field, and each read needed an address add).
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][NSTAGE][TILE];
 
   // ---- work item: XCD-major, KV-head-major, heavy row blocks first ----
   // A workgroup holds hw query heads of one KV head (hw divides G, at most 4)
@@ -281,8 +285,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
   }
   // instruction pair i (one K and one V load) of this wave's share of a tile
   auto dma_part = [&](int kb, int buf, int i) {
-    uint16_t* kdst = &lds[buf][0] + 512 * (NDMA * w + i);
-    uint16_t* vdst = &lds[buf][TILE] + 512 * (NDMA * w + i);
+    uint16_t* kdst = &lds[0][buf][0] + 512 * (NDMA * w + i);
+    uint16_t* vdst = &lds[1][buf][0] + 512 * (NDMA * w + i);
     if (kb + BN - 1 <= kv_hi) {
       const char* kbase = reinterpret_cast<const char*>(Kg) + kb * krow_b;
       const char* vbase = reinterpret_cast<const char*>(Vg) + kb * vrow_b;
@@ -370,8 +374,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
   };
   const int kr0 = key_of_m(n);                        // this lane's K row in a sub-tile
 
-  const lds_u8* const lbase = (const lds_u8*)(lds_void*)&lds[0][0];
-  constexpr int kStage = 2 * TILE * 2;  // bytes of one K + V stage
+  const lds_u8* const lbase = (const lds_u8*)(lds_void*)&lds[0][0][0];
+  constexpr int kStage = TILE * 2;             // bytes of one K (or V) tile
+  constexpr int kVBase = NSTAGE * TILE * 2;    // byte offset of the V tiles
   constexpr int kSubBytes = 2 * 32 * D;  // bytes of one 32-key sub-tile of K
   // Per-lane LDS byte offsets of the K operand reads of stage 0, sub-tile 0, one
   // per k-step (chunk 2 ks + h2 of row kr0); the other sub-tile and stage are
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int chunk = 4 * db + 2 * (tg & 1) + (tc >> 1);
-      vrd[db] = 2 * TILE + 2 * D * key0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
+      vrd[db] = kVBase + 2 * D * key0 + 16 * (chunk ^ vrow_swz<D>(key0)) + 8 * (tc & 1);
     }
   }
 
