@@ -395,7 +395,7 @@ gqa_status gqa_append_kv_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t 
  * cache), turns each 16-key unit into the plan's 16-bit type in LDS (exact),
  * folds each KV head's k_scale into the softmax scale and its v_scale into
  * the normalization.  Needs a bf16 or fp16 plan of head size 64, 128 or 256
- * (UNSUPPORTED otherwise); no caller mask.
+ * (UNSUPPORTED otherwise); a caller mask goes through gqa_decode_int8_masked.
  * Errors: as gqa_decode, INVALID_ARG for NULL scales, UNSUPPORTED for other
  *   plans or more than 2048 row tiles. */
 gqa_status gqa_decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
@@ -418,6 +418,21 @@ gqa_status gqa_decode_fp8_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64
                                  const int32_t* seqlens_k, const float* head_sink,
                                  float k_scale, float v_scale, const gqa_mask* mask,
                                  void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* gqa_decode_int8 with a caller mask over [B, Hq, curr, capacity], as for
+ * gqa_decode_masked ("Attention Kernel Design", section "Layouts and
+ * semantics": boolean or additive attention_bias broadcast over batch and
+ * heads).  An additive value is added to the scaled logit of the dequantized
+ * K (before softcap), whatever the head's k_scale.  The mask's data and
+ * strides must be multiples of 4 bytes (boolean) or 16 bytes and 4 elements
+ * (additive), as for gqa_decode_fp8_masked.
+ * Errors: as gqa_decode_int8 and gqa_decode_masked; INVALID_ARG for a NULL
+ *   mask; UNSUPPORTED for another mask layout or a rolling cache. */
+gqa_status gqa_decode_int8_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                  gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                  const int32_t* seqlens_k, const float* head_sink,
+                                  const float* k_scales, const float* v_scales, const gqa_mask* mask,
+                                  void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* The kernel that computed the attention of this thread's last call, so a
  * caller can tell a fast path from the slow one (the pages' streaming path

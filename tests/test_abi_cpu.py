@@ -337,6 +337,23 @@ def test_int8_validation():
     assert dec(hh=hf) == B.GQA_ERR_UNSUPPORTED and "INT8" in B.gqa_last_error()
     assert dec(Bn=0) == B.GQA_OK
 
+    # with a caller mask: INT8 caches have only the matrix-core decode
+    def dm(mask, hh=h, Bn=2, ks=sc):
+        return B.gqa_decode_int8_masked(hh, Bn, 1, 64, t(), c8, c8, t(), s, None, ks, sc, mask,
+                                        ctypes.c_void_p(FAKE), ws, None)
+    ok = B.gqa_mask(FAKE, 0, 0, 64, B.GQA_MASK_BOOL)
+    assert dm(None) == B.GQA_ERR_INVALID_ARG and "mask" in B.gqa_last_error()
+    assert dm(ok, ks=None) == B.GQA_ERR_INVALID_ARG and "scales" in B.gqa_last_error()
+    assert dm(B.gqa_mask(FAKE + 2, 0, 0, 64, B.GQA_MASK_BOOL)) == B.GQA_ERR_UNSUPPORTED
+    assert "INT8" in B.gqa_last_error()
+    assert dm(B.gqa_mask(FAKE + 8, 0, 0, 64, B.GQA_MASK_ADDITIVE)) == B.GQA_ERR_UNSUPPORTED
+    assert dm(B.gqa_mask(FAKE, 0, 0, 66, B.GQA_MASK_ADDITIVE)) == B.GQA_ERR_UNSUPPORTED
+    assert dm(B.gqa_mask(FAKE, 0, 0, 64, 3)) == B.GQA_ERR_INVALID_ARG and "kind" in B.gqa_last_error()
+    assert dm(ok, hh=hf) == B.GQA_ERR_UNSUPPORTED and "INT8" in B.gqa_last_error()
+    hr = plan(rolling_cache=1, local_window_size=8)
+    assert dm(ok, hh=hr) == B.GQA_ERR_UNSUPPORTED and "rolling" in B.gqa_last_error()
+    assert dm(ok, Bn=0) == B.GQA_OK
+
 
 def test_last_path_is_none_after_failed_or_empty_calls():
     h = plan()

@@ -1,6 +1,6 @@
 """INT8 KV caches with per-KV-head scales on the GPU (gqa_append_kv_int8,
-gqa_decode_int8) against the oracle's INT8 cache (oracle.int8), on the same
-seeded inputs.
+gqa_decode_int8, gqa_decode_int8_masked) against the oracle's INT8 cache
+(oracle.int8), on the same seeded inputs.
 
 Quantization is integer work: the cached codes must equal the oracle's bit
 for bit, over every 16-bit value, with different scales per KV head.  Decode
@@ -185,3 +185,52 @@ def test_int8_decode_rolling(gpu):
                                  oracle.int8.dequantize(vr.astype(np.int8), vs.numpy()), s, scale=w.sm_scale,
                                  window=W, softcap=30.0, head_sink=to_f64(d["head_sink"]))
     compare(out, want, "bf16", "rolling int8 decode")
+
+
+@pytest.mark.parametrize("dtype,D,curr,cap,kind,softcap", [
+    ("bf16", 128, 1, 1024, "bool", 0.0),
+    ("bf16", 256, 4, 600, "add", 50.0),
+    ("f16", 64, 3, 800, "add", 0.0),
+    ("f16", 64, 2, 300, "bool", 5.0),
+])
+def test_int8_decode_with_mask_matches_oracle(gpu, dtype, D, curr, cap, kind, softcap):
+    """gqa_decode_int8_masked against the oracle's attention over the
+    dequantized caches with the same mask: an additive value joins the scaled
+    logit of the dequantized K whatever the head's k_scale (the scales differ
+    by up to 5x between heads here), and a row whose mask removes every key
+    is 0."""
+    B, Hq, Hkv = 3, 8, 2
+    seq = [cap - 1, 17, cap // 2]
+    w = Workload("i8mask", "decode", dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, Lq=curr, Lk=cap,
+                 window=-1 if D != 256 else 200, softcap=softcap, smooth_softmax=True,
+                 seqlens=("list", seq), seed=850 + D + curr)
+    d = generate(w)
+    ks = torch.tensor([0.012, 0.06], dtype=torch.float32)
+    vs = _scales(Hkv, D + 2, 0.01, 0.05)
+    rng = np.random.default_rng(D + cap + 1)
+    shape = (B, Hq, curr, cap)
+    if kind == "bool":
+        mask = torch.from_numpy(rng.random(shape) < 0.6)
+        mask[1, 3] = False
+    else:
+        m = (rng.standard_normal(shape) * 2.0).astype(np.float32)
+        m[rng.random(shape) < 0.05] = -np.inf
+        m[1, 3] = -np.inf
+        mask = torch.from_numpy(m)
+    kc0 = torch.from_numpy(rng.integers(-127, 128, (B, Hkv, cap, D)).astype(np.int8))
+    vc0 = torch.from_numpy(rng.integers(-127, 128, (B, Hkv, cap, D)).astype(np.int8))
+    plan = make_plan(w)
+    kc, vc = kc0.cuda(), vc0.cuda()
+    seq_d = d["seqlens_k"].cuda()
+    plan.append_kv_int8(d["k_new"].cuda(), d["v_new"].cuda(), kc, vc, seq_d, ks.cuda(), vs.cuda())
+    out = plan.decode_int8(d["q"].cuda(), kc, vc, seq_d, ks.cuda(), vs.cuda(), mask=mask.cuda())
+    torch.cuda.synchronize()
+    s = np.asarray(seq, dtype=np.int64)
+    kc_o, vc_o = oracle.int8.append(kc0.numpy(), vc0.numpy(), to_f64(d["k_new"]), to_f64(d["v_new"]), s,
+                                    ks.numpy(), vs.numpy())
+    assert np.array_equal(kc.cpu().numpy(), kc_o) and np.array_equal(vc.cpu().numpy(), vc_o)
+    want = oracle.int8.decode(to_f64(d["q"]), kc_o, vc_o, s, k_scales=ks.numpy(), v_scales=vs.numpy(),
+                              scale=w.sm_scale, window=w.window, softcap=softcap, smooth_softmax=True,
+                              mask=mask.numpy() if kind == "bool" else mask.numpy().astype(np.float64))
+    compare(out, want, dtype, f"int8 masked decode {dtype} D={D} curr={curr} {kind}")
+    assert not out[1, 3].any(), "a head whose mask removes every key must give 0"

@@ -35,7 +35,7 @@ EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
             "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_append_decode", "gqa_prefill_rotary",
             "gqa_last_path", "gqa_last_error", "gqa_probe_mfma_peak",
-            "gqa_append_kv_int8", "gqa_decode_int8")
+            "gqa_append_kv_int8", "gqa_decode_int8", "gqa_decode_int8_masked")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
 
@@ -135,6 +135,8 @@ def load():
     lib.gqa_append_kv_int8.restype = ctypes.c_int
     lib.gqa_decode_int8.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P, P, P, S, P]
     lib.gqa_decode_int8.restype = ctypes.c_int
+    lib.gqa_decode_int8_masked.argtypes = [gqa_plan_t, I32, I32, I64, T, T, T, T, P, P, P, P, MK, P, S, P]
+    lib.gqa_decode_int8_masked.restype = ctypes.c_int
     lib.gqa_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P]
     lib.gqa_probe_mfma_peak.restype = ctypes.c_int
     lib.gqa_last_path.argtypes = []
@@ -259,6 +261,14 @@ def gqa_decode_int8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k
                     workspace, ws_bytes, stream) -> int:
     return load().gqa_decode_int8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink,
                                   k_scales, v_scales, workspace, ws_bytes, stream)
+
+
+def gqa_decode_int8_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scales,
+                           v_scales, mask, workspace, ws_bytes, stream) -> int:
+    return load().gqa_decode_int8_masked(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k,
+                                         head_sink, k_scales, v_scales,
+                                         None if mask is None else ctypes.byref(mask),
+                                         workspace, ws_bytes, stream)
 
 
 def gqa_probe_mfma_peak(blocks, iters, stamps, sink, stream) -> int:
@@ -679,17 +689,25 @@ class Plan:
                                  _ptr(v_scales), _stream(stream)))
 
     def decode_int8(self, q, k_cache, v_cache, seqlens_k, k_scales, v_scales, out=None, *, head_sink=None,
-                    workspace=None, stream=None):
+                    workspace=None, mask=None, stream=None):
+        """``mask``: bool or float32, broadcastable to [B, Hq, curr, capacity]."""
         import torch
         self._check_dtype(q, out)
         self._int8_args(k_cache, v_cache, k_scales, v_scales)
-        self._decode_args(q, k_cache, v_cache, seqlens_k, out, head_sink, workspace, None, torch.int8)
+        self._decode_args(q, k_cache, v_cache, seqlens_k, out, head_sink, workspace, mask, torch.int8)
         _same_device(q, k_scales=k_scales, v_scales=v_scales)
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
             workspace = self.new_workspace(q.device)
         B, _, curr, _ = q.shape
+        if mask is not None:
+            m = self.mask_view(mask, B, curr, k_cache.shape[2])
+            check(gqa_decode_int8_masked(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_cache),
+                                         tensor_view(v_cache), tensor_view(out), _ptr(seqlens_k), _ptr(head_sink),
+                                         _ptr(k_scales), _ptr(v_scales), m, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+            return out
         check(gqa_decode_int8(self._h, B, curr, k_cache.shape[2], tensor_view(q), tensor_view(k_cache),
                               tensor_view(v_cache), tensor_view(out), _ptr(seqlens_k), _ptr(head_sink),
                               _ptr(k_scales), _ptr(v_scales), _ptr(workspace),

@@ -692,6 +692,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     const float kq = KVQ == 2 ? a.k_scales[x.g] : 1.0f;
     const float c_l2p = SOFTCAP ? 1.0f : c_l2 * kq;
     const float soc = a.scale_over_cap * kq;
+    // an additive mask value in this head's code-score units
+    const float bmul = KVQ == 2 ? a.bias_mul / kq : a.bias_mul;
 
     // this lane's query row (padding rows carry zeros and are never stored)
     const int my_r = kRowsPerTile * x.rt + n;
@@ -926,7 +928,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float x = sc[r];
-          if constexpr (MASK == 2) x = fmaf(mf_cur[r], a.bias_mul, x);
+          if constexpr (MASK == 2) x = fmaf(mf_cur[r], bmul, x);
           sc[r] = a.cap_log2 * tanh_fast(x * soc);
         }
       }
@@ -946,7 +948,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       if constexpr (MASK == 2) {  // -inf (or NaN) removes the key
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          sc[r] = mf_cur[r] > -INFINITY ? (SOFTCAP ? sc[r] : fmaf(mf_cur[r], a.bias_mul, sc[r])) : -INFINITY;
+          sc[r] = mf_cur[r] > -INFINITY ? (SOFTCAP ? sc[r] : fmaf(mf_cur[r], bmul, sc[r])) : -INFINITY;
       }
       // online softmax: lanes n, n+16, n+32, n+48 share row n
       float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -1106,8 +1108,13 @@ auto visit_d(const AttnArgs& a, bool softcap, const Op& op) {
   if (a.fuse_append)  // 16-bit caches, no mask (the host guarantees both)
     return softcap ? op.template run<IS_BF16, D, true, 0, 0, true>()
                    : op.template run<IS_BF16, D, false, 0, 0, true>();
-  if (a.kv_fp8 == 2)  // INT8 caches, no mask (the host guarantees it)
+  if (a.kv_fp8 == 2) {  // INT8 caches
+    if (a.mask_kind == 1)
+      return softcap ? op.template run<IS_BF16, D, true, 1, 2>() : op.template run<IS_BF16, D, false, 1, 2>();
+    if (a.mask_kind == 2)
+      return softcap ? op.template run<IS_BF16, D, true, 2, 2>() : op.template run<IS_BF16, D, false, 2, 2>();
     return softcap ? op.template run<IS_BF16, D, true, 0, 2>() : op.template run<IS_BF16, D, false, 0, 2>();
+  }
   if (a.kv_fp8) {
     if (a.mask_kind == 1)
       return softcap ? op.template run<IS_BF16, D, true, 1, 1>() : op.template run<IS_BF16, D, false, 1, 1>();

@@ -913,11 +913,11 @@ GQA_API gqa_status gqa_append_kv_int8(gqa_plan_t plan, int32_t B, int32_t curr, 
                     "append_kv_int8 launch");
 }
 
-GQA_API gqa_status gqa_decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
-                                   gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
-                                   const int32_t* seqlens_k, const float* head_sink, const float* k_scales,
-                                   const float* v_scales, void* workspace, size_t ws_bytes, void* hip_stream) {
-  g_path = GQA_PATH_NONE;
+namespace {
+gqa_status decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                       gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out, const int32_t* seqlens_k,
+                       const float* head_sink, const float* k_scales, const float* v_scales, const gqa_mask* mask,
+                       void* workspace, size_t ws_bytes, void* hip_stream) {
   if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
   if (B < 0 || curr < 0 || capacity < 0) return fail(GQA_ERR_INVALID_ARG, "B, curr and capacity must be >= 0");
   if (B > plan->max_batch) return fail(GQA_ERR_CAPACITY, "B = %d exceeds the plan's max_batch %d", B, plan->max_batch);
@@ -932,6 +932,20 @@ GQA_API gqa_status gqa_decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int
   if (k_scales == nullptr || v_scales == nullptr) return fail(GQA_ERR_INVALID_ARG, "k_scales and v_scales are required");
   if ((st = check_sink(plan, head_sink)) != GQA_OK) return st;
   if ((st = check_ring(plan, curr, capacity)) != GQA_OK) return st;
+  if (mask != nullptr && plan->attrs.rolling_cache)
+    return fail(GQA_ERR_UNSUPPORTED, "a decode mask indexes keys by position: not with a rolling cache");
+  gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
+  if (mask != nullptr) {
+    if ((st = set_mask(a, mask)) != GQA_OK) return st;
+    // the matrix-core decode reads a lane's 4 mask entries of a unit as one
+    // aligned load; INT8 caches have no other kernel
+    const bool boolean = mask->kind == GQA_MASK_BOOL;
+    if (reinterpret_cast<uintptr_t>(mask->data) % (boolean ? 4 : 16) != 0 || mask->stride_b % 4 != 0 ||
+        mask->stride_h % 4 != 0 || mask->stride_q % 4 != 0)
+      return fail(GQA_ERR_UNSUPPORTED,
+                  "INT8 caches need a mask whose data and strides are multiples of %d bytes and 4 elements",
+                  boolean ? 4 : 16);
+  }
   if (B == 0 || curr == 0) return GQA_OK;
   if (seqlens_k == nullptr) return fail(GQA_ERR_INVALID_ARG, "seqlens_k is NULL");
   const int esz = elem_size(plan->attrs.dtype);
@@ -939,12 +953,12 @@ GQA_API gqa_status gqa_decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int
   if ((st = check_tensor("k_cache", k_cache, 1)) != GQA_OK) return st;
   if ((st = check_tensor("v_cache", v_cache, 1)) != GQA_OK) return st;
   if ((st = check_tensor("out", out, esz)) != GQA_OK) return st;
-  gqa::AttnArgs a = make_args(plan, q, k_cache, v_cache, out, B, curr, capacity, 1);
   a.seqlens = seqlens_k;
   a.head_sink = head_sink;
   a.kv_fp8 = 2;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
+  a.bias_mul = 1.0f / plan->scale;  // divided by the head's k_scale in the kernel (code-score units)
   gqa::DecodeGeometry geo = gqa::decode_geometry(B, a.Hkv, a.G, curr, a.D);
   const size_t need = geo.ws_floats * sizeof(float);
   if (workspace == nullptr || ws_bytes < need)
@@ -956,6 +970,27 @@ GQA_API gqa_status gqa_decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int
   return hip_status(path_decode_mfma(a, (int)plan->attrs.dtype, plan->attrs.softcap > 0, geo,
                                      reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(hip_stream)),
                     "decode_int8 launch");
+}
+}  // namespace
+
+GQA_API gqa_status gqa_decode_int8(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity, gqa_tensor q,
+                                   gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                   const int32_t* seqlens_k, const float* head_sink, const float* k_scales,
+                                   const float* v_scales, void* workspace, size_t ws_bytes, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
+  return decode_int8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scales, v_scales,
+                     nullptr, workspace, ws_bytes, hip_stream);
+}
+
+GQA_API gqa_status gqa_decode_int8_masked(gqa_plan_t plan, int32_t B, int32_t curr, int64_t capacity,
+                                          gqa_tensor q, gqa_tensor k_cache, gqa_tensor v_cache, gqa_tensor out,
+                                          const int32_t* seqlens_k, const float* head_sink, const float* k_scales,
+                                          const float* v_scales, const gqa_mask* mask, void* workspace,
+                                          size_t ws_bytes, void* hip_stream) {
+  g_path = GQA_PATH_NONE;
+  if (mask == nullptr) return fail(GQA_ERR_INVALID_ARG, "mask is NULL");
+  return decode_int8(plan, B, curr, capacity, q, k_cache, v_cache, out, seqlens_k, head_sink, k_scales, v_scales,
+                     mask, workspace, ws_bytes, hip_stream);
 }
 
 GQA_API const char* gqa_last_error(void) { return g_err.c_str(); }
