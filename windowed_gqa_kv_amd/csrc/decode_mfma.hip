@@ -428,6 +428,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds[kRowsPerTile * 2 * D];  // Q tile, swizzled like K
   __shared__ int pre[kMaxTiles + 2];  // unit prefix sum over tiles (then workgroups per tile)
   __shared__ int wsum[4];
+  __shared__ int split_s[5];  // U, Gs, slice start and end, first tile (T <= 64)
   __shared__ int flag[256];
   // (q_off, valid, lo, hi) of each tile, kept by the setup when there are
   // few tiles, so that starting a piece needs no memory round trip
@@ -501,52 +502,6 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     }
   };
   const bool cached = T <= kCachedTiles;
-  int U;
-  // With at most 64 row tiles, lane t of every wave keeps tile t's unit count
-  // and prefix sums in registers, and the split below works on them without
-  // LDS round trips (the same values every wave; wave 0 publishes them).
-  const bool small = T <= 64;
-  int my_ut = 0, my_pre = 0, my_nt = 0, my_pren = 0;
-  if (small) {
-    // one tile per lane: every wave scans in registers on its own (no
-    // barriers inside the scan); wave 0 publishes the prefix sums
-    Tile x{};
-    int ut = 0;
-    if (lane < T) {
-      x = make_tile(a, rows, nrt, lane, MASK != 0);
-      ut = units_of(x);
-    }
-    const int incl = wave_incl_scan(ut, lane);
-    U = __builtin_amdgcn_readlane(incl, 63);
-    my_ut = ut;
-    my_pre = incl - ut;
-    if (w == 0) {
-      if (lane == 0) pre[0] = 0;
-      if (lane < T) {
-        pre[lane + 1] = incl;
-        if (cached) tcache[lane] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
-      }
-    }
-    __syncthreads();
-  } else {
-    block_scan(pre, [&](int t) {
-      const Tile x = make_tile(a, rows, nrt, t, MASK != 0);
-      if (cached) tcache[t] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
-      return units_of(x);
-    });
-    U = pre[T];
-  }
-
-  // tiles nobody streams (no allowed key for any of their rows) output zeros
-  for (int t = k; t < T; t += G) {
-    if (pre[t + 1] != pre[t]) continue;
-    const Tile x = make_tile(a, rows, nrt, t, MASK != 0);
-    for (int idx = tid; idx < x.rows_tile * (D / 4); idx += 256) {
-      const int row = kRowsPerTile * x.rt + idx / (D / 4);
-      store_row4<IS_BF16, D>(a, x.b, x.g * a.G + row % a.G, row / a.G, 4 * (idx % (D / 4)), f32x4{});
-    }
-  }
-
   // Slices.  With at least two workgroups per row tile, tile t gets
   // n_t = ceil(u_t / L) workgroups of its own (u_t its units, L the smallest
   // load for which they fit the grid) and its units are cut evenly among them:
@@ -557,37 +512,133 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   // are consecutive.
   const bool aligned = 2 * T <= G;
   int* const pren = pre + T + 1;  // aligned: prefix sum of n_t (2T + 2 <= kMaxTiles + 2 entries)
-  int Gs;
-  if (aligned) {
-    // L = ceil(U / (G - T)) always fits, since sum_t ceil(u_t / L) < U / L + T
-    int lo = max(1, (U + G - 1) / G), hi = max(1, (U + (G - T) - 1) / (G - T));
-    // every wave runs the search on its own (same result, no barriers)
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      int c = 0;
-      if (small)
-        c = (my_ut + mid - 1) / mid;  // 0 in lanes past the last tile
-      else
-        for (int t = lane; t < T; t += 64) c += (pre[t + 1] - pre[t] + mid - 1) / mid;
-      if (wave_sum(c, lane) <= G) hi = mid; else lo = mid + 1;
-    }
-    const int L = lo;
-    if (small) {
-      my_nt = (my_ut + L - 1) / L;
-      const int nincl = wave_incl_scan(my_nt, lane);
-      my_pren = nincl - my_nt;
-      Gs = __builtin_amdgcn_readlane(nincl, 63);
-      if (w == 0) {
-        if (lane == 0) pren[0] = 0;
-        if (lane < T) pren[lane + 1] = nincl;
+  int U, Gs, ustart, uend, t_first;
+  if (T <= 64) {
+    // One tile per lane of wave 0, which computes the whole split in
+    // registers (no LDS round trips, no barriers inside) and publishes it;
+    // the other waves wait at one barrier.  The split is integer work on
+    // the scalar unit, which all waves of a CU share: when every wave
+    // computed it, the first K/V request came ~1.5 us later.
+    if (w == 0) {
+      Tile x{};
+      int ut = 0;
+      if (lane < T) {
+        x = make_tile(a, rows, nrt, lane, MASK != 0);
+        ut = units_of(x);
       }
-      __syncthreads();  // pren[] is read by the arrivals at the end
-    } else {
+      const int incl = wave_incl_scan(ut, lane);
+      const int u_all = __builtin_amdgcn_readlane(incl, 63);
+      const int pre_l = incl - ut;  // pre[lane]
+      if (lane == 0) pre[0] = 0;
+      if (lane < T) {
+        pre[lane + 1] = incl;
+        if (cached) tcache[lane] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
+      }
+      int g_used, us = 0, ue = 0, tf = 0;
+      if (aligned) {
+        // L = ceil(U / (G - T)) always fits, since sum_t ceil(u_t / L) < U / L + T
+        int lo = max(1, (u_all + G - 1) / G), hi = max(1, (u_all + (G - T) - 1) / (G - T));
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (wave_sum((ut + mid - 1) / mid, lane) <= G) hi = mid; else lo = mid + 1;  // 0 past the last tile
+        }
+        const int nt = (ut + lo - 1) / lo;
+        const int nincl = wave_incl_scan(nt, lane);
+        const int pren_l = nincl - nt;  // pren[lane]
+        g_used = __builtin_amdgcn_readlane(nincl, 63);
+        if (lane == 0) pren[0] = 0;
+        if (lane < T) pren[lane + 1] = nincl;  // read by the arrivals at the end
+        if (k < g_used) {
+          // the largest t with pren[t] <= k (a prefix of the lanes; never an empty tile)
+          tf = 63 - __builtin_clzll(__ballot(lane < T && pren_l <= k));
+          const int u_t = __builtin_amdgcn_readlane(ut, tf);
+          const int p_t = __builtin_amdgcn_readlane(pre_l, tf);
+          const int n_t = __builtin_amdgcn_readlane(nt, tf);
+          const int i = k - __builtin_amdgcn_readlane(pren_l, tf);
+          us = p_t + mul_div(u_t, i, n_t);
+          ue = p_t + mul_div(u_t, i + 1, n_t);
+        }
+      } else {
+        g_used = min(G, u_all);
+        if (k < g_used) {
+          us = mul_div(u_all, k, g_used);
+          ue = mul_div(u_all, k + 1, g_used);
+          // first tile holding unit us: the largest t with pre[t] <= us
+          tf = 63 - __builtin_clzll(__ballot(lane < T && pre_l <= us));
+        }
+      }
+      if (lane == 0) {
+        split_s[0] = u_all;
+        split_s[1] = g_used;
+        split_s[2] = us;
+        split_s[3] = ue;
+        split_s[4] = tf;
+      }
+    }
+    __syncthreads();
+    U = split_s[0];
+    Gs = split_s[1];
+    ustart = split_s[2];
+    uend = split_s[3];
+    t_first = split_s[4];
+  } else {
+    block_scan(pre, [&](int t) {
+      const Tile x = make_tile(a, rows, nrt, t, MASK != 0);
+      if (cached) tcache[t] = int4{x.sp.q_off, x.sp.valid, x.lo, x.hi};
+      return units_of(x);
+    });
+    U = pre[T];
+    if (aligned) {
+      // L = ceil(U / (G - T)) always fits, since sum_t ceil(u_t / L) < U / L + T
+      int lo = max(1, (U + G - 1) / G), hi = max(1, (U + (G - T) - 1) / (G - T));
+      // every wave runs the search on its own (same result, no barriers)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        int c = 0;
+        for (int t = lane; t < T; t += 64) c += (pre[t + 1] - pre[t] + mid - 1) / mid;
+        if (wave_sum(c, lane) <= G) hi = mid; else lo = mid + 1;
+      }
+      const int L = lo;
       block_scan(pren, [&](int t) { return (pre[t + 1] - pre[t] + L - 1) / L; });
       Gs = pren[T];
+      ustart = uend = t_first = 0;
+      if (k < Gs) {
+        int lo2 = 0, hi2 = T;  // invariant: pren[lo2] <= k < pren[hi2]
+        while (hi2 - lo2 > 1) {
+          const int mid = (lo2 + hi2) >> 1;
+          if (pren[mid] <= k) lo2 = mid; else hi2 = mid;
+        }
+        t_first = lo2;
+        const int ut = pre[lo2 + 1] - pre[lo2];
+        const int n = pren[lo2 + 1] - pren[lo2], i = k - pren[lo2];
+        ustart = pre[lo2] + mul_div(ut, i, n);
+        uend = pre[lo2] + mul_div(ut, i + 1, n);
+      }
+    } else {
+      Gs = min(G, U);
+      ustart = uend = t_first = 0;
+      if (k < Gs) {
+        ustart = mul_div(U, k, Gs);
+        uend = mul_div(U, k + 1, Gs);
+        // first tile holding unit ustart: the largest t with pre[t] <= ustart
+        int lo2 = 0, hi2 = T;  // invariant: pre[lo2] <= ustart < pre[hi2]
+        while (hi2 - lo2 > 1) {
+          const int mid = (lo2 + hi2) >> 1;
+          if (pre[mid] <= ustart) lo2 = mid; else hi2 = mid;
+        }
+        t_first = lo2;
+      }
     }
-  } else {
-    Gs = min(G, U);
+  }
+
+  // tiles nobody streams (no allowed key for any of their rows) output zeros
+  for (int t = k; t < T; t += G) {
+    if (pre[t + 1] != pre[t]) continue;
+    const Tile x = make_tile(a, rows, nrt, t, MASK != 0);
+    for (int idx = tid; idx < x.rows_tile * (D / 4); idx += 256) {
+      const int row = kRowsPerTile * x.rt + idx / (D / 4);
+      store_row4<IS_BF16, D>(a, x.b, x.g * a.G + row % a.G, row / a.G, 4 * (idx % (D / 4)), f32x4{});
+    }
   }
   if constexpr (FUSE) {
     // the fused append's stores (the loads above have long returned)
@@ -607,39 +658,6 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       nvalid = owner_of(pre[t + 1] - 1, U, Gs) - first + 1;
     }
   };
-
-  int ustart, uend, t_first;
-  if (aligned && small) {
-    // the largest t with pren[t] <= k (a prefix of the lanes; never an empty tile)
-    t_first = 63 - __builtin_clzll(__ballot(lane < T && my_pren <= k));
-    const int ut = __builtin_amdgcn_readlane(my_ut, t_first);
-    const int pt = __builtin_amdgcn_readlane(my_pre, t_first);
-    const int n = __builtin_amdgcn_readlane(my_nt, t_first);
-    const int i = k - __builtin_amdgcn_readlane(my_pren, t_first);
-    ustart = pt + mul_div(ut, i, n);
-    uend = pt + mul_div(ut, i + 1, n);
-  } else if (aligned) {
-    int lo = 0, hi = T;  // invariant: pren[lo] <= k < pren[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pren[mid] <= k) lo = mid; else hi = mid;
-    }
-    t_first = lo;
-    const int ut = pre[lo + 1] - pre[lo];
-    const int n = pren[lo + 1] - pren[lo], i = k - pren[lo];
-    ustart = pre[lo] + mul_div(ut, i, n);
-    uend = pre[lo] + mul_div(ut, i + 1, n);
-  } else {
-    ustart = mul_div(U, k, Gs);
-    uend = mul_div(U, k + 1, Gs);
-    // first tile holding unit ustart: the largest t with pre[t] <= ustart
-    int lo = 0, hi = T;  // invariant: pre[lo] <= ustart < pre[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= ustart) lo = mid; else hi = mid;
-    }
-    t_first = lo;
-  }
   int t_last = t_first - 1;  // last tile this workgroup touches
 
   const float c_l2 = SOFTCAP ? 1.0f : a.scale_log2;
@@ -685,8 +703,9 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     } else {
       x = make_tile(a, rows, nrt, t, MASK != 0);
     }
-    const int c_lo = x.lo + kSub * ua;
-    const int c_hi = min(x.hi, x.lo + kSub * ub - 1);
+    // the piece's key range (wave-uniform: scalar registers)
+    const int c_lo = __builtin_amdgcn_readfirstlane(x.lo + kSub * ua);
+    const int c_hi = __builtin_amdgcn_readfirstlane(min(x.hi, x.lo + kSub * ub - 1));
     // INT8 caches: the KV head's K scale joins the softmax scale (raw scores
     // are in code units)
     const float kq = KVQ == 2 ? a.k_scales[x.g] : 1.0f;
@@ -711,7 +730,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     // step's new rows
     const KT* __restrict__ Kn = reinterpret_cast<const KT*>(a.k_new) + x.b * a.kn_sb + x.g * a.kn_sh;
     const KT* __restrict__ Vn = reinterpret_cast<const KT*>(a.v_new) + x.b * a.vn_sb + x.g * a.vn_sh;
-    const int new_lo = x.sp.valid - a.Lq;
+    const int new_lo = __builtin_amdgcn_readfirstlane(x.sp.valid - a.Lq);
 
     // Q tile -> LDS by DMA, shared by the 4 waves (instruction i by wave i % 4).
     // Padding rows load the tile's last real row (in bounds, finite); MFMA
@@ -737,12 +756,57 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     // every key.  Caches that are not rings take the plain addresses (a
     // wave-uniform branch per unit).
     const int turns = a.ring ? c_lo - c_lo % a.ring : 0;
-    // Rows past the piece end are clamped to its last key (a real key,
-    // finite, masked out for every query row): no per-lane branches.
+    // A unit whose 16 rows are consecutive cache rows (the usual case) is
+    // loaded from a scalar base, its first row, plus a per-lane 32-bit offset
+    // built from full-rate integer operations: lane chunk 64 i + lane is row
+    // kRowsDma i + lr, chunk lc (swizzled on 16-bit caches).  The row strides
+    // are below 2^24 elements (the host sends larger ones to the streaming
+    // kernel), so every offset fits 32 bits.  Per-lane 64-bit row addresses
+    // cost six quarter-rate multiplies per K/V load pair.
+    constexpr int kChunksDma = KV8 ? D / 16 : RG::kSlots;  // 16-byte chunks per streamed row
+    constexpr int kRowsDma = 64 / kChunksDma;               // rows per wave-wide load
+    const int lr = lane / kChunksDma, lc = lane % kChunksDma;
+    const uint32_t rbk = (uint32_t)a.k_ss * (uint32_t)sizeof(KT);
+    const uint32_t rbv = (uint32_t)a.v_ss * (uint32_t)sizeof(KT);
+    const uint32_t lane_k = (uint32_t)lr * rbk, lane_v = (uint32_t)lr * rbv;
+    // Other units (the piece ends inside them, they reach the step's new
+    // rows, or they wrap around a rolling cache) take per-lane row
+    // addresses; rows past the piece end are clamped to its last key (a real
+    // key, finite, masked out for every query row): no per-lane branches.
     auto issue_t = [&](int s, int j, auto ring_tag, auto fuse_tag) {
       const int kb = c_lo + kSub * (w + 4 * j);
       unsigned char* kdst = my_ring + s * 2 * RG::kInBytes;
       unsigned char* vdst = kdst + RG::kInBytes;
+      int s0 = kb;  // the slot of the unit's first row
+      bool whole = kb + kSub - 1 <= c_hi;
+      if constexpr (decltype(fuse_tag)::value) whole = whole && kb + kSub - 1 < new_lo;
+      if constexpr (decltype(ring_tag)::value) {
+        s0 -= turns;
+        s0 = s0 >= a.ring ? s0 - a.ring : s0;
+        whole = whole && s0 + kSub - 1 < a.ring;
+      }
+      // (not in the fused step at head size 256, whose registers are full:
+      // the extra path spills it)
+      constexpr bool kWholeUnits = !(FUSE && D >= 256);
+      if (kWholeUnits && whole) {
+        const char* kbase = reinterpret_cast<const char*>(Kg + (int64_t)s0 * a.k_ss);
+        const char* vbase = reinterpret_cast<const char*>(Vg + (int64_t)s0 * a.v_ss);
+        // the offsets are rebuilt per unit (a few full-rate operations):
+        // hoisted out of the loop they would hold 4 * kDmaPerUnit registers
+        uint32_t lk = lane_k, lv = lane_v;
+        asm volatile("" : "+v"(lk), "+v"(lv));
+#pragma unroll
+        for (int i = 0; i < RG::kDmaPerUnit; ++i) {
+          const uint32_t c16 = 16u * (uint32_t)(KV8 ? lc : lc ^ swz<D>(kRowsDma * i + lr));
+          __builtin_amdgcn_global_load_lds(
+              (global_void*)(kbase + (size_t)((uint32_t)(kRowsDma * i) * rbk) + (size_t)(lk + c16)),
+              (lds_void*)(kdst + 1024 * i), 16, 0, kNonTemporal);
+          __builtin_amdgcn_global_load_lds(
+              (global_void*)(vbase + (size_t)((uint32_t)(kRowsDma * i) * rbv) + (size_t)(lv + c16)),
+              (lds_void*)(vdst + 1024 * i), 16, 0, kNonTemporal);
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < RG::kDmaPerUnit; ++i) {
         const int pos = 64 * i + lane;                 // 16-byte chunk position in the unit
