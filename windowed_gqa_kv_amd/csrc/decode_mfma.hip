@@ -423,7 +423,6 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   constexpr int MERGE = D / 4 + 2;                            // floats per lane in a merge slot
   // The rings hold the LDS stages while streaming and the wave merge slots
   // between pieces.
-  static_assert(2 * MERGE * 64 * 4 <= kWaves * RG::kWaveBytes, "merge slots fit the rings");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kWaves * RG::kWaveBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds[kRowsPerTile * 2 * D];  // Q tile, swizzled like K
   __shared__ int pre[kMaxTiles + 2];  // unit prefix sum over tiles (then workgroups per tile)
@@ -1051,48 +1050,58 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     }
 
     // ---- merge the 4 waves through LDS (lane-to-lane: identical layouts) ----
-    auto put = [&](int slot) {
-      float* ml = merge_lds[slot];
+    // Every wave writes its state to its slot (accumulators as one 16-byte
+    // entry per lane and output block, then m and l); after one barrier,
+    // wave w merges the four states of output blocks [w DB/4, (w+1) DB/4)
+    // and stores them to the partial, and wave 0 also stores the rows'
+    // maxima and sums.  (A tree of two halving steps put three barriers and
+    // four serial LDS passes between the last unit and the stores.)
+    static_assert(kWaves * MERGE * 64 * 4 <= kWaves * RG::kWaveBytes, "merge slots fit the rings");
+    static_assert(DB % kWaves == 0, "whole output blocks per wave");
+    constexpr int DBW = DB / kWaves;
+    __syncthreads();  // every wave's last unit is consumed: the rings are free
+    {
+      float* ml = merge_lds[w];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ml[(4 * db + r) * 64 + lane] = o[db][r];
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(ml + 4 * (db * 64 + lane)) = o[db];
       ml[(D / 4) * 64 + lane] = m_run;
       ml[(D / 4 + 1) * 64 + lane] = l_run;
-    };
-    auto take = [&](int slot) {
-      const float* ml = merge_lds[slot];
-      const float m_b = ml[(D / 4) * 64 + lane];
-      const float l_b = ml[(D / 4 + 1) * 64 + lane];
-      const float M = fmaxf(m_run, m_b);
-      if (M == -INFINITY) return;
-      const float fa = fast_exp2((m_run - M) * c_l2p);
-      const float fb = fast_exp2((m_b - M) * c_l2p);
-      l_run = l_run * fa + l_b * fb;
-      m_run = M;
+    }
+    __syncthreads();
+    {
+      float mv[kWaves], lv[kWaves];
+      float M = -INFINITY;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int i = 0; i < kWaves; ++i) {
+        mv[i] = merge_lds[i][(D / 4) * 64 + lane];
+        lv[i] = merge_lds[i][(D / 4 + 1) * 64 + lane];
+        M = fmaxf(M, mv[i]);
+      }
+      float f[kWaves];
+      float l_m = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * fa + ml[(4 * db + r) * 64 + lane] * fb;
-    };
-    __syncthreads();
-    if (w >= 2) put(w - 2);
-    __syncthreads();
-    if (w < 2) take(w);
-    __syncthreads();
-    if (w == 1) put(0);
-    __syncthreads();
-    if (w == 0) {
-      take(0);
-      float l_row = l_run + xor16(l_run);
+      for (int i = 0; i < kWaves; ++i) {
+        f[i] = mv[i] == -INFINITY ? 0.0f : fast_exp2((mv[i] - M) * c_l2p);  // 0 for an empty state
+        l_m += lv[i] * f[i];
+      }
+      f32x4 om[DBW];
+#pragma unroll
+      for (int q = 0; q < DBW; ++q) {
+        const int db = DBW * w + q;
+        om[q] = f32x4{};
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i)
+          om[q] += *reinterpret_cast<const f32x4*>(merge_lds[i] + 4 * (db * 64 + lane)) * f[i];
+      }
+      float l_row = l_m + xor16(l_m);
       l_row += xor32(l_row);
       if (row_ok) {
         float* p = part + (int64_t)(k + t) * PART;  // slot k + t: unique per piece
         const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(p, 0, PART * 4, kRawBufferWord3);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) coherent_store4(pr, 4 * (n * D + 16 * db + 4 * q4), o[db]);
-        if (q4 == 0) {
-          coherent_store(p + kRowsPerTile * D + n, m_run == -INFINITY ? -INFINITY : m_run * c_l2p);
+        for (int q = 0; q < DBW; ++q) coherent_store4(pr, 4 * (n * D + 16 * (DBW * w + q) + 4 * q4), om[q]);
+        if (w == 0 && q4 == 0) {
+          coherent_store(p + kRowsPerTile * D + n, M == -INFINITY ? -INFINITY : M * c_l2p);
           coherent_store(p + kRowsPerTile * D + kRowsPerTile + n, l_row);
         }
       }
