@@ -34,6 +34,18 @@ CXXFLAGS = [
 ]
 
 
+# Per-source flags.  The decode keeps its output accumulators in VGPRs across
+# units (the lazy rescale multiplies them on the vector ALU); with the MFMA
+# results in AGPRs the compiler copied all of them to AGPRs around every
+# unit's P V MFMAs (32 copies and their wait states per unit at head size
+# 128).  gfx950 MFMAs read and write VGPRs directly, and every decode
+# instance fits 256 VGPRs that way.  The prefill keeps the default: at head
+# size 256 it needs AGPRs.
+FILE_FLAGS = {
+    "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -47,7 +59,7 @@ def sources():
 
 def _compile(cc, src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [cc, *CXXFLAGS, "-c", src, "-o", obj]
+    cmd = [cc, *CXXFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
