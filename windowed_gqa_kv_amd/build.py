@@ -34,15 +34,17 @@ CXXFLAGS = [
 ]
 
 
-# Per-source flags.  The decode keeps its output accumulators in VGPRs across
-# units (the lazy rescale multiplies them on the vector ALU); with the MFMA
-# results in AGPRs the compiler copied all of them to AGPRs around every
-# unit's P V MFMAs (32 copies and their wait states per unit at head size
-# 128).  gfx950 MFMAs read and write VGPRs directly, and every decode
-# instance fits 256 VGPRs that way.  The prefill keeps the default: at head
-# size 256 it needs AGPRs.
+# Per-source flags: MFMA results in VGPRs.  Both kernels keep their output
+# accumulators in VGPRs across tiles / units (the lazy rescale multiplies
+# them on the vector ALU); with the MFMA results in AGPRs the compiler copied
+# them to AGPRs around every P V step (the decode: 32 copies and their wait
+# states per unit at head size 128; the head-size-256 prefill: 500-650 copies
+# each way in a kernel body, and its additive-mask instances spilled).  gfx950
+# MFMAs read and write VGPRs directly; AGPRs are still used where a kernel
+# needs more than 256 registers (the head-size-256 prefill).
 FILE_FLAGS = {
     "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
