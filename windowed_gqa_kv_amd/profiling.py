@@ -35,11 +35,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 
 def src_hash(names) -> str:
-    """Short hash of kernel sources under csrc/ (bench.py compares it)."""
+    """Short hash of kernel sources under csrc/ and of their per-file compiler
+    flags (bench.py compares it): a record taken on other code is ignored."""
+    from .build import FILE_FLAGS
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(PKG, "csrc", n), "rb") as f:
             h.update(f.read())
+        h.update(" ".join(FILE_FLAGS.get(n, [])).encode())
     return h.hexdigest()[:16]
 
 
