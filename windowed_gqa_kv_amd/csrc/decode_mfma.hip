@@ -446,9 +446,8 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   // ---- the step's append, fused: new row t of (b, g) into the cache slot of
   // position total_b - curr + t (mod the ring), with the skip rule of the
   // append kernel.  Its 16-byte chunks are spread over the whole grid, a few
-  // threads per workgroup.  A thread's first chunk is loaded here and stored
-  // once the split below is known, so no wave waits for the loads.  Nobody
-  // reads these slots in this launch. ----
+  // threads of waves 1-3 per workgroup.  Nobody reads these slots in this
+  // launch. ----
   constexpr int kAppendChunks = D / 8;
   const int ap_items = FUSE ? a.B * a.Hkv * a.Lq * kAppendChunks : 0;
   u32x4 ap_k = u32x4{}, ap_v = u32x4{};
@@ -480,8 +479,17 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     *reinterpret_cast<u32x4*>(kc + b * a.k_sb + g * a.k_sh + slot * a.k_ss + 8 * c) = kx;
     *reinterpret_cast<u32x4*>(vc + b * a.v_sb + g * a.v_sh + slot * a.v_ss + 8 * c) = vx;
   };
-  if constexpr (FUSE)
-    if (k + G * tid < ap_items) ap_load(k + G * tid, ap_k, ap_v);
+  // Waves 1-3 do the whole append at the start, while wave 0 alone
+  // computes the split below: nothing in the append waits for the split,
+  // and wave 0's path to the first K/V request stays free of it.
+  if constexpr (FUSE) {
+    if (w > 0) {
+      for (int i = k + G * (tid - 64); i < ap_items; i += G * (256 - 64)) {
+        ap_load(i, ap_k, ap_v);
+        ap_store(i, ap_k, ap_v);
+      }
+    }
+  }
 
   // ---- the split of the work (the same in every workgroup) ----
   // Exclusive prefix sum of f(t) over the row tiles into out[0..T].
@@ -637,13 +645,6 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     for (int idx = tid; idx < x.rows_tile * (D / 4); idx += 256) {
       const int row = kRowsPerTile * x.rt + idx / (D / 4);
       store_row4<IS_BF16, D>(a, x.b, x.g * a.G + row % a.G, row / a.G, 4 * (idx % (D / 4)), f32x4{});
-    }
-  }
-  if constexpr (FUSE) {
-    // the fused append's stores (the loads above have long returned)
-    for (int i = k + G * tid; i < ap_items; i += G * 256) {
-      if (i != k + G * tid) ap_load(i, ap_k, ap_v);
-      ap_store(i, ap_k, ap_v);
     }
   }
   if (k >= Gs) return;
