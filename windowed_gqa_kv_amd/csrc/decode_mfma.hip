@@ -759,16 +759,18 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
     // A unit whose 16 rows are consecutive cache rows (the usual case) is
     // loaded from a scalar base, its first row, plus a per-lane 32-bit offset
     // built from full-rate integer operations: lane chunk 64 i + lane is row
-    // kRowsDma i + lr, chunk lc (swizzled on 16-bit caches).  The row strides
-    // are below 2^24 elements (the host sends larger ones to the streaming
-    // kernel), so every offset fits 32 bits.  Per-lane 64-bit row addresses
-    // cost six quarter-rate multiplies per K/V load pair.
+    // kRowsDma i + lr, chunk lc (swizzled on 16-bit caches).  With row
+    // strides below 2^24 elements every such offset fits 32 bits (at most 16
+    // rows of 2^25 bytes); larger strides take the per-lane path.  Per-lane
+    // 64-bit row addresses cost six quarter-rate multiplies per K/V load
+    // pair.
     constexpr int kChunksDma = KV8 ? D / 16 : RG::kSlots;  // 16-byte chunks per streamed row
     constexpr int kRowsDma = 64 / kChunksDma;               // rows per wave-wide load
     const int lr = lane / kChunksDma, lc = lane % kChunksDma;
     const uint32_t rbk = (uint32_t)a.k_ss * (uint32_t)sizeof(KT);
     const uint32_t rbv = (uint32_t)a.v_ss * (uint32_t)sizeof(KT);
     const uint32_t lane_k = (uint32_t)lr * rbk, lane_v = (uint32_t)lr * rbv;
+    const bool small_strides = a.k_ss < (int64_t(1) << 24) && a.v_ss < (int64_t(1) << 24);
     // Other units (the piece ends inside them, they reach the step's new
     // rows, or they wrap around a rolling cache) take per-lane row
     // addresses; rows past the piece end are clamped to its last key (a real
@@ -778,7 +780,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       unsigned char* kdst = my_ring + s * 2 * RG::kInBytes;
       unsigned char* vdst = kdst + RG::kInBytes;
       int s0 = kb;  // the slot of the unit's first row
-      bool whole = kb + kSub - 1 <= c_hi;
+      bool whole = small_strides && kb + kSub - 1 <= c_hi;
       if constexpr (decltype(fuse_tag)::value) whole = whole && kb + kSub - 1 < new_lo;
       if constexpr (decltype(ring_tag)::value) {
         s0 -= turns;
