@@ -275,21 +275,25 @@ __device__ __forceinline__ void lse_combine(float& M, float& Ls, f32x4 (&acc)[QP
   M = Mn;
 }
 
-// Merge of one row tile's split partials by one wave (no barriers, no LDS):
+// Merge of one row tile's split partials by MW waves of a workgroup, wave cw
+// over the cw-th 1 / MW of the columns (no LDS: every wave reads all maxima
+// and sums, which its factors need, and only its own accumulator columns):
 // log-sum-exp over the splits, sink folded into the denominator, normalised,
-// narrowed with round-to-nearest-even and stored.  Split x of the tile is the
-// partial at gpart + x * PART (acc [16][D], then 16 maxima in log2 units,
-// then 16 sums).  The tile's rows are padded to Rp = 2^lrp and each row gets
-// 64 / Rp lanes; a lane owns QPL output quads of its row (a chunk) and merges
-// them over its splits, NB splits in flight at once.  Only when a row has
-// more lanes than quads (one or two rows) do several lanes share a chunk as
-// split groups, combined with shuffles at the end.
-template <bool IS_BF16, int D, int QPL>
+// narrowed with round-to-nearest-even and stored.
+// Split x of the tile is the partial at gpart + x * PART (acc [16][D], then
+// 16 maxima in log2 units, then 16 sums).  The tile's rows are padded to
+// Rp = 2^lrp and each row gets 64 / Rp lanes; a lane owns QPL output quads of
+// its row (a chunk) and merges them over its splits, NB splits in flight at
+// once.  Where a row has more lanes than the wave's quads, several lanes
+// share a chunk as split groups, combined with shuffles at the end.
+template <bool IS_BF16, int D, int QPL, int MW>
 __device__ __forceinline__ void merge_tile_q(const AttnArgs& a, int lrp, int R, int rt, int xb, int xg,
-                                             const float* __restrict__ gpart, int nvalid, int lane) {
+                                             const float* __restrict__ gpart, int nvalid, int lane, int cw) {
   constexpr int PART = kRowsPerTile * D + 2 * kRowsPerTile;
   constexpr int Q4 = D / 4;  // output quads per row
-  constexpr int NC = Q4 / QPL;  // chunks per row
+  constexpr int NCA = Q4 / QPL;  // chunks per row
+  constexpr int NC = NCA / MW;   // chunks per row of this wave (from cw NC on)
+  static_assert(NCA % MW == 0, "whole chunks per wave");
   // splits per lane in flight: 64 loaded quads per lane, or 128 at D = 256,
   // whose kernel runs one workgroup per CU and has the registers to spare
   constexpr int NB = (D >= 256 ? 32 : 16) / QPL;
@@ -306,7 +310,7 @@ __device__ __forceinline__ void merge_tile_q(const AttnArgs& a, int lrp, int R, 
   const int h = xg * a.G + row % a.G;
   const float sink = a.use_sink ? sink_log2(a, h) : 0.0f;
   // NC / CL passes, the same number in every lane and wave
-  for (int c = sub % CL; c < NC; c += CL) {
+  for (int c = cw * NC + sub % CL; c < (cw + 1) * NC; c += CL) {
     float M = -INFINITY, Ls = 0.0f;
     f32x4 acc[QPL];
 #pragma unroll
@@ -384,26 +388,24 @@ __device__ __forceinline__ void merge_tile_q(const AttnArgs& a, int lrp, int R, 
 
 // Quads per lane for a tile of R rows: the row's lanes (64 / Rp) cover its
 // D / 4 output quads once where they can, at most 8 quads per lane.
-template <bool IS_BF16, int D>
+// The caller has acquired the other workgroups' partials (see the arrivals).
+template <bool IS_BF16, int D, int MW>
 __device__ __forceinline__ void merge_tile(const AttnArgs& a, int rows, int nrt, int tt,
-                                           const float* __restrict__ gpart, int nvalid, int lane) {
-  // the other workgroups' write-through stores were complete before their
-  // arrivals, which this workgroup has seen: acquire once before reading
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                                           const float* __restrict__ gpart, int nvalid, int lane, int cw) {
   // the tile's coordinates (no lengths needed here)
   const int bg = tt / nrt, rt = tt - bg * nrt;
   const int xb = bg / a.Hkv, xg = bg - xb * a.Hkv;
   const int R = min(kRowsPerTile, rows - kRowsPerTile * rt);
   const int lrp = R <= 1 ? 0 : (R <= 2 ? 1 : (R <= 4 ? 2 : (R <= 8 ? 3 : 4)));  // log2 of padded rows
-  const int qpl = ((D / 4) << lrp) / 64;  // quads of a row / lanes of a row
+  const int qpl = ((D / 4 / MW) << lrp) / 64;  // this wave's quads of a row / lanes of a row
   if (qpl <= 1)
-    merge_tile_q<IS_BF16, D, 1>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
+    merge_tile_q<IS_BF16, D, 1, MW>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane, cw);
   else if (qpl == 2)
-    merge_tile_q<IS_BF16, D, 2>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
+    merge_tile_q<IS_BF16, D, 2, MW>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane, cw);
   else if (qpl == 4)
-    merge_tile_q<IS_BF16, D, 4>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
+    merge_tile_q<IS_BF16, D, 4, MW>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane, cw);
   else
-    merge_tile_q<IS_BF16, D, 8>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane);
+    merge_tile_q<IS_BF16, D, 8, MW>(a, lrp, R, rt, xb, xg, gpart, nvalid, lane, cw);
 }
 
 // MASK = 1 / 2: a caller boolean (uint8) / additive (fp32) mask over
@@ -1133,21 +1135,39 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
       flag[tid] = f;
     }
     __syncthreads();
-    // The tiles this workgroup completed go to its waves in turn, so that
-    // their merges run side by side.
+    // The other workgroups' device-scope stores were complete before their
+    // arrivals, which this workgroup has seen; a merging wave acquires them
+    // (an L2 invalidate) before it reads.  Below head size 256 each tile
+    // this workgroup completed goes to one wave, in turn, so that merges run
+    // side by side.  At head size 256 (partials of 16.5 KB, one workgroup
+    // per CU) every wave merges a quarter of the columns of each tile: wave
+    // 0 acquires once and the barrier orders the other waves' loads after
+    // it (an acquire per wave measured slower than one wave per tile; at
+    // head size 128 the split merge is ~1 us slower, at 256 ~1.8 us faster).
+    constexpr int MW = D >= 256 ? kWaves : 1;
+    if constexpr (MW > 1) {
+      bool any = false;
+      for (int c0 = 0; c0 < nbt; c0 += 64) any |= __ballot(c0 + lane < nbt && flag[c0 + lane]) != 0;
+      if (any) {  // the same in every wave (flag[] is shared)
+        if (w == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
+      }
+    }
     int cnt = 0;
     for (int c0 = 0; c0 < nbt; c0 += 64) {
       uint64_t mask = __ballot(c0 + lane < nbt && flag[c0 + lane]);
       while (mask) {
         const int i = c0 + __builtin_ctzll(mask);
         mask &= mask - 1;
-        if (cnt++ % kWaves != w) continue;
+        if (MW == 1 && cnt++ % kWaves != w) continue;
         const int tt = base + i;
         int first, nvalid;
         contributors(tt, first, nvalid);
         nvalid = min(nvalid, Gs - first);  // never past the slots this call wrote
-        merge_tile<IS_BF16, D>(a, rows, nrt, tt, part + (int64_t)(first + tt) * PART, nvalid, lane);
-        if (lane == 0)  // ready for the next call
+        if constexpr (MW == 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        merge_tile<IS_BF16, D, MW>(a, rows, nrt, tt, part + (int64_t)(first + tt) * PART, nvalid, lane,
+                                   MW == 1 ? 0 : w);
+        if ((MW == 1 || w == 0) && lane == 0)  // ready for the next call
           __hip_atomic_store(&counters[tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
