@@ -150,7 +150,7 @@ def test_prefill_sweep(gpu, dt, D, Lq, Lk, W):
 
 DECODE_SWEEP = []
 for dt, D in (("f32", 64), ("bf16", 64), ("bf16", 128), ("bf16", 256), ("f16", 128)):
-    for curr in (1, 2, 3, 4, 16):
+    for curr in (1, 2, 3, 4, 16, 40):
         for G in (1, 4, 8):
             for W in (-1, 1, 5, 300):
                 DECODE_SWEEP.append((dt, D, curr, G, W))
