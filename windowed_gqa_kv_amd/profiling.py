@@ -17,6 +17,11 @@
         KEY and stamped with a hash of the kernel sources, is merged into the
         JSON file FILE, where bench.py looks it up.
 
+    python -m windowed_gqa_kv_amd.profiling counters DIR [DIR ...] --kernel PATTERN [--grid N]
+        Markdown table of the mean per-dispatch value of every counter found in
+        the DIRs' counter runs, over the kernels whose names contain PATTERN
+        (and whose grid holds N work-items), with the dispatch count.
+
 The sources that the hash covers are the ones bench.py names; a record taken
 on other sources is ignored there.
 """
@@ -94,6 +99,12 @@ def counter_mean(d: str, counter: str, pattern: str, grid: int = 0):
     return sum(vals.values()) / len(vals), len(vals)
 
 
+def counter_names(d: str):
+    """Counter names present in a counter run."""
+    with open(_one(os.path.join(d, "**", "*counter_collection.csv"))) as f:
+        return sorted({r["Counter_Name"] for r in csv.DictReader(f)})
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -107,7 +118,20 @@ def main(argv=None):
     t.add_argument("--sources", default="decode_mfma.hip,common.h,kernels.h")
     t.add_argument("--command", default="")
     t.add_argument("--grid", type=int, default=0)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--grid", type=int, default=0)
     a = ap.parse_args(argv)
+
+    if a.cmd == "counters":
+        print("| counter | mean per dispatch | dispatches |")
+        print("|---|---|---|")
+        for d in a.dirs:
+            for name in counter_names(d):
+                mean, n = counter_mean(d, name, a.kernel, a.grid)
+                print(f"| {name} | {mean:,.0f} | {n} |")
+        return 0
 
     if a.cmd == "stats" and a.by_grid:
         print("| kernel | grid work-items | calls | avg us | min us | max us |")
