@@ -212,11 +212,51 @@ def bench_decode(w, steps, warmup, replicas):
     fused_ms = b2b(step)
     dec_ms = b2b(lambda r: plan.decode(q, caches[r][0], caches[r][1], seq, out, head_sink=sink, workspace=ws))
     s = d["seqlens_k"].numpy()
+    stream = kv_stream_ceiling(w, s, caches, b2b) if w.D == 128 and w.dtype != "f32" else None
     dec_bytes = work.decode_bytes(s, w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window)
     app_bytes = work.append_bytes(w.B, w.Hkv, w.Lq, w.D, w.dtype)
     return dict(ms_per_step=ms, two_launch_ms_per_step=ms_two, eager_ms_per_step=eager_ms,
                 step_bytes=dec_bytes + app_bytes, kernel_ms=fused_ms, kernel_ms_events_each=step_ms_events_each,
-                decode_only_ms=dec_ms, decode_bytes=dec_bytes, replicas=R, inputs=d)
+                decode_only_ms=dec_ms, decode_bytes=dec_bytes, replicas=R, inputs=d, stream=stream)
+
+
+def kv_stream_ceiling(w, seqlens, caches, b2b):
+    """The decode's own K/V units (16 keys from each tile's first allowed key
+    on, K and V) streamed by the library's probe through the decode's
+    loading scheme, with no attention work, at the decode's grid, timed like
+    the decode (back to back over the cache replicas): the rate this loading
+    scheme reaches on these bytes."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    from windowed_gqa_kv_amd import binding
+
+    offs = []
+    for b in range(w.B):
+        valid = int(seqlens[b]) + 1
+        q_off = valid - w.Lq
+        lo = 0 if w.window < 0 else max(0, q_off - w.window + 1)
+        n_units = (valid - 1 - lo) // 16 + 1
+        for g in range(w.Hkv):
+            base = (b * w.Hkv + g) * w.Lk + lo
+            offs.extend((base + 16 * u) * 256 for u in range(n_units))
+    off = torch.tensor(np.array(offs, dtype=np.int64), device="cuda")
+    sink = torch.zeros(1, device="cuda")
+    kv_bytes = caches[0][0].numel() * caches[0][0].element_size()
+    grid = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    U = len(offs)
+
+    def probe(r):
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rc = binding.gqa_probe_kv_stream(grid, ctypes.c_void_p(caches[r][0].data_ptr()),
+                                         ctypes.c_void_p(caches[r][1].data_ptr()), kv_bytes,
+                                         ctypes.c_void_p(off.data_ptr()), U, ctypes.c_void_p(sink.data_ptr()), stream)
+        if rc != 0:
+            raise RuntimeError(f"K/V stream probe failed ({rc})")
+
+    ms = b2b(probe)
+    return dict(kernel_ms=ms, units=U, bytes=U * 2 * 16 * 256, grid=grid)
 
 
 def bench_prefill(w, steps, warmup, d=None):
@@ -755,6 +795,14 @@ def main():
                                      "frac": round(dec_only / PEAK_HBM_GBS, 4),
                                      "traffic": _traffic("decode", w.name, dec_src)}},
     }
+    if r["stream"] is not None:
+        st = r["stream"]
+        rate = st["bytes"] / (st["kernel_ms"] / 1e3) / 1e9
+        line["roofline"]["stream_ceiling"] = {
+            "kernel": "kv_stream_probe_kernel (the decode's K/V units through its LDS-DMA loading scheme, "
+                      "no attention work)",
+            "units": st["units"], "grid": st["grid"], "kernel_ms": round(st["kernel_ms"], 5),
+            "bytes_per_launch": st["bytes"], "achieved": round(rate, 2), "frac": round(rate / PEAK_HBM_GBS, 4)}
 
     if not args.no_extra:
         extra = []

@@ -34,7 +34,7 @@ EXPORTED = ("gqa_plan", "gqa_plan_destroy", "gqa_workspace_size", "gqa_prefill",
             "gqa_append_kv", "gqa_decode", "gqa_apply_rotary", "gqa_append_kv_rotary",
             "gqa_prefill_masked", "gqa_decode_masked", "gqa_append_kv_fp8", "gqa_decode_fp8",
             "gqa_decode_fp8_masked", "gqa_decode_noalloc", "gqa_append_decode", "gqa_prefill_rotary",
-            "gqa_last_path", "gqa_last_error", "gqa_probe_mfma_peak",
+            "gqa_last_path", "gqa_last_error", "gqa_probe_mfma_peak", "gqa_probe_kv_stream",
             "gqa_append_kv_int8", "gqa_decode_int8", "gqa_decode_int8_masked")
 GQA_MASK_BOOL, GQA_MASK_ADDITIVE = 1, 2
 
@@ -139,6 +139,8 @@ def load():
     lib.gqa_decode_int8_masked.restype = ctypes.c_int
     lib.gqa_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P]
     lib.gqa_probe_mfma_peak.restype = ctypes.c_int
+    lib.gqa_probe_kv_stream.argtypes = [ctypes.c_int, P, P, I64, P, ctypes.c_int, P, P]
+    lib.gqa_probe_kv_stream.restype = ctypes.c_int
     lib.gqa_last_path.argtypes = []
     lib.gqa_last_path.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
@@ -275,6 +277,12 @@ def gqa_probe_mfma_peak(blocks, iters, stamps, sink, stream) -> int:
     """Measurement aid (include/gqa_probe.h): back-to-back bf16 MFMAs with
     shader-clock and 100 MHz stamps per wave."""
     return load().gqa_probe_mfma_peak(blocks, iters, stamps, sink, stream)
+
+
+def gqa_probe_kv_stream(grid, k, v, kv_bytes, unit_off, units, sink, stream) -> int:
+    """Measurement aid (include/gqa_probe.h): K/V units streamed through the
+    decode's loading scheme with no attention work."""
+    return load().gqa_probe_kv_stream(grid, k, v, kv_bytes, unit_off, units, sink, stream)
 
 
 def gqa_last_error() -> str:
