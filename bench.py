@@ -212,7 +212,7 @@ def bench_decode(w, steps, warmup, replicas):
     fused_ms = b2b(step)
     dec_ms = b2b(lambda r: plan.decode(q, caches[r][0], caches[r][1], seq, out, head_sink=sink, workspace=ws))
     s = d["seqlens_k"].numpy()
-    stream = kv_stream_ceiling(w, s, caches, b2b) if w.D == 128 and w.dtype != "f32" else None
+    stream = kv_stream_ceiling(w, s, caches, b2b) if w.D in (128, 256) and w.dtype != "f32" else None
     dec_bytes = work.decode_bytes(s, w.Lq, w.Hq, w.Hkv, w.D, w.dtype, w.causal, w.window)
     app_bytes = work.append_bytes(w.B, w.Hkv, w.Lq, w.D, w.dtype)
     return dict(ms_per_step=ms, two_launch_ms_per_step=ms_two, eager_ms_per_step=eager_ms,
@@ -220,18 +220,28 @@ def bench_decode(w, steps, warmup, replicas):
                 decode_only_ms=dec_ms, decode_bytes=dec_bytes, replicas=R, inputs=d, stream=stream)
 
 
+def _ceiling(st):
+    rate = st["bytes"] / (st["kernel_ms"] / 1e3) / 1e9
+    return {"kernel": "kv_stream_probe_kernel (the decode's K/V units through its LDS-DMA loading scheme, "
+                      "no attention work)",
+            "units": st["units"], "grid": st["grid"], "kernel_ms": round(st["kernel_ms"], 5),
+            "bytes_per_launch": st["bytes"], "achieved": round(rate, 2), "frac": round(rate / PEAK_HBM_GBS, 4)}
+
+
 def kv_stream_ceiling(w, seqlens, caches, b2b):
     """The decode's own K/V units (16 keys from each tile's first allowed key
     on, K and V) streamed by the library's probe through the decode's
-    loading scheme, with no attention work, at the decode's grid, timed like
-    the decode (back to back over the cache replicas): the rate this loading
-    scheme reaches on these bytes."""
+    loading scheme, with no attention work, at the decode's workgroups per CU
+    (two at head size 128, one at 256), timed like the decode (back to back
+    over the cache replicas): the rate this loading scheme reaches on these
+    bytes."""
     import ctypes
 
     import numpy as np
     import torch
     from windowed_gqa_kv_amd import binding
 
+    row_bytes = 2 * w.D
     offs = []
     for b in range(w.B):
         valid = int(seqlens[b]) + 1
@@ -240,23 +250,23 @@ def kv_stream_ceiling(w, seqlens, caches, b2b):
         n_units = (valid - 1 - lo) // 16 + 1
         for g in range(w.Hkv):
             base = (b * w.Hkv + g) * w.Lk + lo
-            offs.extend((base + 16 * u) * 256 for u in range(n_units))
+            offs.extend((base + 16 * u) * row_bytes for u in range(n_units))
     off = torch.tensor(np.array(offs, dtype=np.int64), device="cuda")
     sink = torch.zeros(1, device="cuda")
     kv_bytes = caches[0][0].numel() * caches[0][0].element_size()
-    grid = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    grid = (2 if w.D == 128 else 1) * torch.cuda.get_device_properties(0).multi_processor_count
     U = len(offs)
 
     def probe(r):
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        rc = binding.gqa_probe_kv_stream(grid, ctypes.c_void_p(caches[r][0].data_ptr()),
+        rc = binding.gqa_probe_kv_stream(grid, row_bytes, ctypes.c_void_p(caches[r][0].data_ptr()),
                                          ctypes.c_void_p(caches[r][1].data_ptr()), kv_bytes,
                                          ctypes.c_void_p(off.data_ptr()), U, ctypes.c_void_p(sink.data_ptr()), stream)
         if rc != 0:
             raise RuntimeError(f"K/V stream probe failed ({rc})")
 
     ms = b2b(probe)
-    return dict(kernel_ms=ms, units=U, bytes=U * 2 * 16 * 256, grid=grid)
+    return dict(kernel_ms=ms, units=U, bytes=U * 2 * 16 * row_bytes, grid=grid)
 
 
 def bench_prefill(w, steps, warmup, d=None):
@@ -796,13 +806,7 @@ def main():
                                      "traffic": _traffic("decode", w.name, dec_src)}},
     }
     if r["stream"] is not None:
-        st = r["stream"]
-        rate = st["bytes"] / (st["kernel_ms"] / 1e3) / 1e9
-        line["roofline"]["stream_ceiling"] = {
-            "kernel": "kv_stream_probe_kernel (the decode's K/V units through its LDS-DMA loading scheme, "
-                      "no attention work)",
-            "units": st["units"], "grid": st["grid"], "kernel_ms": round(st["kernel_ms"], 5),
-            "bytes_per_launch": st["bytes"], "achieved": round(rate, 2), "frac": round(rate / PEAK_HBM_GBS, 4)}
+        line["roofline"]["stream_ceiling"] = _ceiling(r["stream"])
 
     if not args.no_extra:
         extra = []
@@ -822,6 +826,8 @@ def main():
                                        "decode_only": {"kernel_ms": round(r4["decode_only_ms"], 5),
                                                        "achieved": round(d4, 2),
                                                        "frac": round(d4 / PEAK_HBM_GBS, 4)}}})
+            if r4["stream"] is not None:
+                extra[-1]["roofline"]["stream_ceiling"] = _ceiling(r4["stream"])
             del r4
         for wid in (3, 5):
             wp = WORKLOADS[wid]

@@ -23,8 +23,9 @@ int gqa_probe_mfma_peak(int blocks, int iters, void* stamps, void* sink, void* h
 
 /* Streams `units` K/V units through the split-KV decode's loading scheme with
  * no attention work: the ceiling its HBM rate is read against.  A unit is 16
- * key rows of 256 bytes (head size 128, 16-bit elements) of k and the same
- * bytes of v, at byte offset unit_off[u] (device int64 [units]) in both; the
+ * key rows of row_bytes bytes (256: head size 128, 512: head size 256, with
+ * 16-bit elements) of k and the same bytes of v, at byte offset unit_off[u]
+ * (device int64 [units]) in both; the
  * units are cut evenly over `grid` workgroups of 4 waves, and each wave
  * streams its share through two LDS stages by LDS DMA (non-temporal, the
  * decode's chunk swizzle), waiting for each unit as the decode does.
@@ -32,10 +33,10 @@ int gqa_probe_mfma_peak(int blocks, int iters, void* stamps, void* sink, void* h
  * unit would leave it reads the first unit instead.  sink is a device fp32
  * [1] that keeps the reads (practically never written).  The caller times
  * the launch (events on hip_stream).  Returns 0, 1 for a bad argument (grid
- * < 1, a NULL buffer, kv_bytes < 4096, or more than 256 units per
- * workgroup), 4 for a launch error. */
-int gqa_probe_kv_stream(int grid, const void* k, const void* v, int64_t kv_bytes, const int64_t* unit_off,
-                        int units, void* sink, void* hip_stream);
+ * < 1, row_bytes other than 256 or 512, a NULL buffer, kv_bytes below one
+ * unit, or more than 256 units per workgroup), 4 for a launch error. */
+int gqa_probe_kv_stream(int grid, int row_bytes, const void* k, const void* v, int64_t kv_bytes,
+                        const int64_t* unit_off, int units, void* sink, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -36,24 +36,28 @@ def test_kv_stream_probe_runs_and_checks_arguments(gpu):
     v = torch.ones(kv_bytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, device="cuda")
     # in-range units, plus offsets outside the buffers (the kernel reads unit 0 for them)
-    offs = [4096 * i for i in range(200)] + [kv_bytes - 4096, -4096, kv_bytes, kv_bytes - 16, 1 << 40]
+    offs = [4096 * i for i in range(200)] + [kv_bytes - 8192, kv_bytes - 4096, -4096, kv_bytes, kv_bytes - 16,
+                                             1 << 40]
     off = torch.tensor(np.array(offs, dtype=np.int64), device="cuda")
     U = len(offs)
-    for grid in (1, 3, 64, 512):
-        assert gpu.gqa_probe_kv_stream(grid, _p(k), _p(v), kv_bytes, _p(off), U, _p(sink), _stream()) == 0
+    for rb in (256, 512):
+        for grid in (1, 3, 64, 512):
+            assert gpu.gqa_probe_kv_stream(grid, rb, _p(k), _p(v), kv_bytes, _p(off), U, _p(sink), _stream()) == 0
     torch.cuda.synchronize()
     assert sink.item() == 0.0
     # no units: nothing streamed
-    assert gpu.gqa_probe_kv_stream(4, _p(k), _p(v), kv_bytes, _p(off), 0, _p(sink), _stream()) == 0
+    assert gpu.gqa_probe_kv_stream(4, 256, _p(k), _p(v), kv_bytes, _p(off), 0, _p(sink), _stream()) == 0
     torch.cuda.synchronize()
     # host-side rejections: no launch
     bad = [
-        (0, _p(k), _p(v), kv_bytes, _p(off), U),          # no workgroups
-        (1, _p(k), _p(v), 4095, _p(off), U),              # a buffer smaller than one unit
-        (1, None, _p(v), kv_bytes, _p(off), U),           # a NULL buffer
-        (1, _p(k), _p(v), kv_bytes, None, U),             # no offsets for the units
-        (1, _p(k), _p(v), kv_bytes, _p(off), 257),        # more than 256 units per workgroup
-        (4, _p(k), _p(v), kv_bytes, _p(off), -1),         # a negative count
+        (0, 256, _p(k), _p(v), kv_bytes, _p(off), U),     # no workgroups
+        (1, 384, _p(k), _p(v), kv_bytes, _p(off), U),     # a row size the probe does not take
+        (1, 256, _p(k), _p(v), 4095, _p(off), U),         # a buffer smaller than one unit
+        (1, 512, _p(k), _p(v), 8191, _p(off), U),
+        (1, 256, None, _p(v), kv_bytes, _p(off), U),      # a NULL buffer
+        (1, 256, _p(k), _p(v), kv_bytes, None, U),        # no offsets for the units
+        (1, 256, _p(k), _p(v), kv_bytes, _p(off), 257),   # more than 256 units per workgroup
+        (4, 256, _p(k), _p(v), kv_bytes, _p(off), -1),    # a negative count
     ]
-    for grid, kp, vp, nb, op, units in bad:
-        assert gpu.gqa_probe_kv_stream(grid, kp, vp, nb, op, units, _p(sink), _stream()) == 1
+    for grid, rb, kp, vp, nb, op, units in bad:
+        assert gpu.gqa_probe_kv_stream(grid, rb, kp, vp, nb, op, units, _p(sink), _stream()) == 1

@@ -139,7 +139,7 @@ def load():
     lib.gqa_decode_int8_masked.restype = ctypes.c_int
     lib.gqa_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P]
     lib.gqa_probe_mfma_peak.restype = ctypes.c_int
-    lib.gqa_probe_kv_stream.argtypes = [ctypes.c_int, P, P, I64, P, ctypes.c_int, P, P]
+    lib.gqa_probe_kv_stream.argtypes = [ctypes.c_int, ctypes.c_int, P, P, I64, P, ctypes.c_int, P, P]
     lib.gqa_probe_kv_stream.restype = ctypes.c_int
     lib.gqa_last_path.argtypes = []
     lib.gqa_last_path.restype = ctypes.c_int
@@ -279,10 +279,11 @@ def gqa_probe_mfma_peak(blocks, iters, stamps, sink, stream) -> int:
     return load().gqa_probe_mfma_peak(blocks, iters, stamps, sink, stream)
 
 
-def gqa_probe_kv_stream(grid, k, v, kv_bytes, unit_off, units, sink, stream) -> int:
-    """Measurement aid (include/gqa_probe.h): K/V units streamed through the
-    decode's loading scheme with no attention work."""
-    return load().gqa_probe_kv_stream(grid, k, v, kv_bytes, unit_off, units, sink, stream)
+def gqa_probe_kv_stream(grid, row_bytes, k, v, kv_bytes, unit_off, units, sink, stream) -> int:
+    """Measurement aid (include/gqa_probe.h): K/V units of 16 rows of
+    row_bytes streamed through the decode's loading scheme with no attention
+    work."""
+    return load().gqa_probe_kv_stream(grid, row_bytes, k, v, kv_bytes, unit_off, units, sink, stream)
 
 
 def gqa_last_error() -> str:
