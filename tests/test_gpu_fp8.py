@@ -64,6 +64,9 @@ CASES = [
     ("bf16", 3, 16, 8, 256, 4, 1200, 500, 50.0, True, [1199, 700, 3], 0.1, 0.1),
     ("f16", 2, 8, 2, 64, 3, 700, -1, 0.0, True, [699, 64], 0.02, 0.05),
     ("bf16", 2, 8, 1, 128, 2, 4096, 1000, 0.0, False, [4095, 2500], 1.0, 0.5),
+    # 40 new rows: several units of new keys, five row tiles per head group
+    ("bf16", 2, 8, 4, 128, 40, 1500, 300, 0.0, True, [1499, 39], 0.05, 0.05),
+    ("f16", 2, 4, 2, 256, 40, 900, -1, 30.0, False, [899, 450], 0.1, 0.02),
 ]
 
 
