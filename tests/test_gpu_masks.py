@@ -123,10 +123,12 @@ def test_masked_prefill_matches_oracle(gpu, case):
     ("f16", 64, 2, 302, "add", 20.0),      # streaming (rows not 16-byte aligned)
     ("bf16", 128, 1, 1022, "bool", 0.0),   # streaming (rows not 4-byte aligned)
     ("f32", 32, 2, 100, "bool", 0.0),      # streaming (fp32)
+    ("bf16", 128, 40, 1024, "bool", 0.0),  # matrix core, 40 new rows (five row tiles per head group)
+    ("bf16", 256, 40, 600, "add", 0.0),    # matrix core, 40 new rows
 ])
 def test_masked_decode_matches_oracle(gpu, dtype, D, curr, cap, kind, softcap):
     B, Hq, Hkv = 3, 8, 2
-    seq = [cap - 1, 17, cap // 2]
+    seq = [cap - 1, max(17, curr - 1), cap // 2]
     w = Workload("maskdec", "decode", dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, Lq=curr, Lk=cap,
                  window=-1 if D != 256 else 200, softcap=softcap,
                  smooth_softmax=True, seqlens=("list", seq), seed=400 + D + curr)
