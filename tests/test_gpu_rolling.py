@@ -26,6 +26,9 @@ CASES = [
     ("f16", 2, 8, 8, 64, 2, 64, 65, [64, 1000], 0.0, False),
     ("f32", 2, 4, 2, 32, 2, 20, 21, [30, 5], 0.0, True),
     ("bf16", 2, 8, 2, 96, 1, 40, 40, [77, 39], 0.0, False),  # generic kernel (head size 96)
+    # 40 new rows, at the smallest ring (W + curr - 1) and past it
+    ("bf16", 2, 8, 2, 128, 40, 200, 239, [5000, 239], 0.0, True),
+    ("bf16", 2, 8, 4, 256, 40, 100, 160, [3000, 1000], 30.0, False),
 ]
 
 
