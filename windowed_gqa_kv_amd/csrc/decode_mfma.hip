@@ -442,7 +442,12 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a, int rows, int n
   const int n = lane & 15;
   const int q4 = lane >> 4;
   const int G = gridDim.x;
-  const int k = blockIdx.x;
+  // The slice this workgroup streams.  Workgroups are dispatched to the 8
+  // XCDs in turn (workgroup b on XCD b mod 8), and a row tile's slices are
+  // consecutive: numbering the slices XCD-major puts each tile's
+  // contributors, its partials and its merge on one XCD (bitwise the same
+  // result; the fused step measured 0.1-0.65 us faster, the rest unchanged).
+  const int k = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int T = a.B * a.Hkv * nrt;
 
   // ---- the step's append, fused: new row t of (b, g) into the cache slot of
